@@ -1,0 +1,22 @@
+"""Single-query GQA decode attention on MI355X: Python binding of libgqa_decode.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the C library (``include/gqa_decode.h``).  PyTorch supplies device
+memory and the stream.  There is no fallback: if the library has not been
+built, importing this package raises.
+"""
+from ._binding import (  # noqa: F401
+    GQA_BF16,
+    GQA_F16,
+    GqaError,
+    Policy,
+    decode,
+    decode_contiguous,
+    lib,
+    library_path,
+    policy_default,
+    policy_pages,
+    status_string,
+    workspace_size,
+    EXPORTED_SYMBOLS,
+)

@@ -1,0 +1,149 @@
+/*
+ * gqa_decode.h -- single-query grouped-query-attention (GQA) decode on one
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: pointers, sizes, no C++ or
+ * framework types.
+ *
+ * What is computed.  For every sequence s and query head i, with
+ * G = h_q / h_kv query heads per KV head and KV head j = floor(i / G):
+ *
+ *     x_t      = scale * <q[s,i,:], K_s[t,:]>          t in [0, L_s)
+ *     out[s,i] = sum_t softmax(x)_t * V_s[t,:]
+ *
+ * (decode-long page, "GQA fused-attention decode kernel -- long context":
+ * the local attention step and "Final normalise + store"; kernel-map page,
+ * VLLM_KERNEL_MAP "paged_attention_v1" for the [num_seqs, num_heads,
+ * head_dim] query layout).  Each (sequence, KV head) token range is cut into
+ * partitions; one workgroup per partition computes the partial triple
+ * (m, l, O) of the decode-long page's tile step for all G query heads at
+ * once, and a second kernel merges the partials with the page's
+ * "_merge_running" rule (kernel-map page, "paged_attention_v2": per
+ * partition reduce, then a cross-partition merge, fp32 max_logits and
+ * exp_sum).  A sequence of at most policy.v1_max_ctx tokens is a single
+ * partition and is written directly (kernel-map page, "paged_attention_v1").
+ *
+ * Layouts (row-major, contiguous, 16-byte aligned base pointers):
+ *   q, out          [num_seqs, h_q, d_head]                    dtype
+ *   paged k, v      [num_blocks, block_size, h_kv, d_head]     dtype
+ *   contiguous k, v [num_seqs, s_kv, h_kv, d_head]             dtype
+ *   block_table     [num_seqs, max_blocks_per_seq]             int32
+ *   ctx_lens        [num_seqs]                                 int32
+ * Token t of sequence s lives in physical block block_table[s, t / block_size],
+ * slot t % block_size.  q, k, v and out share one dtype.
+ *
+ * Numerics.  Q.K^T accumulates in fp32 from exact fp16/bf16 products; the
+ * softmax runs in fp32 in base 2 (log2(e) folded into the scale); softmax
+ * weights enter the P.V product as a two-term (hi + lo) split in the storage
+ * dtype, so the weights carry about 22 (fp16) or 16 (bf16) significant bits;
+ * partials and the merge are fp32; the output is rounded to nearest-even.
+ *
+ * Ownership.  The caller owns every buffer, the workspace included.  The
+ * library never allocates, frees or synchronises and keeps no device state;
+ * calls on different streams with distinct workspaces and outputs may run
+ * concurrently.
+ *
+ * Errors.  Every argument is checked on the host before any HIP call; a
+ * failed check returns its status with nothing launched.  A failed launch
+ * returns GQA_ERR_LAUNCH.  Faults during execution surface at the caller's
+ * next synchronisation of the stream.  Device-resident data the host cannot
+ * see is handled as follows: ctx_lens[s] is clamped to
+ * [0, max_blocks_per_seq * block_size]; a sequence with L_s = 0 gets a zero
+ * output row; block_table entries at or past ceil(L_s / block_size) and
+ * slots at or past L_s are never read; an in-range table entry that names a
+ * block outside the caller's pool is undefined behaviour.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_dtype {
+  GQA_F16 = 0,   /* IEEE binary16 */
+  GQA_BF16 = 1   /* bfloat16 */
+} gqa_dtype_t;
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  GQA_ERR_BAD_SHAPE = 2,    /* a size is negative, zero where it may not be, or inconsistent */
+  GQA_ERR_UNSUPPORTED = 3,  /* valid but not built: d_head, G, block_size or dtype */
+  GQA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment stated above */
+  GQA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than gqa_decode_workspace_size() */
+  GQA_ERR_BAD_POLICY = 6,   /* policy fields out of range */
+  GQA_ERR_BAD_SCALE = 7,    /* scale is NaN or infinite */
+  GQA_ERR_LAUNCH = 8        /* the HIP runtime refused a kernel launch */
+} gqa_status_t;
+
+/*
+ * Launch policy.  partition_size is the number of tokens one workgroup
+ * covers for a split sequence (a multiple of 32 in [32, 1 << 20]);
+ * v1_max_ctx (>= 0) is the longest sequence handled as one partition with no
+ * merge.  The decomposition follows the kernel-map page ("paged_attention_v1"
+ * for short contexts, "paged_attention_v2" above the threshold) with sizes
+ * chosen for MI355X by gqa_policy_default(); gqa_policy_pages() gives the
+ * policy page's AttentionConfig values (partition 512, threshold 8192).
+ * phases selects which kernels a call launches: 0 or 3 = both, 1 = partition
+ * kernel only, 2 = merge kernel only (the merge then reads the partials a
+ * phase-1 call with the same arguments left in the workspace); it exists so
+ * that a caller can time the two kernels apart.
+ */
+typedef struct gqa_policy {
+  int32_t partition_size;
+  int32_t v1_max_ctx;
+  int32_t phases;
+  int32_t reserved;        /* must be 0 */
+} gqa_policy_t;
+
+/* Fill *p with the MI355X default policy. */
+void gqa_policy_default(gqa_policy_t* p);
+/* Fill *p with the policy page's values: partition 512, single pass up to 8192. */
+void gqa_policy_pages(gqa_policy_t* p);
+
+/*
+ * Bytes of workspace gqa_decode / gqa_decode_contiguous need for these sizes
+ * (max_ctx = max_blocks_per_seq * block_size, or s_kv).  0 when no sequence
+ * can be split.  The workspace holds, per (sequence, query head, partition),
+ * the fp32 pair (m, l) and the fp32 un-normalised O row.  policy NULL means
+ * gqa_policy_default().  Returns 0 for invalid arguments.
+ */
+size_t gqa_decode_workspace_size(int num_seqs, int h_q, int d_head, int max_ctx,
+                                 const gqa_policy_t* policy);
+
+/*
+ * Paged decode.  d_head in {64, 128}; 1 <= G = h_q / h_kv <= 16 and h_q a
+ * multiple of h_kv; block_size a power of two in [16, 256]; T_q = 1.
+ * scale multiplies the logits (the workloads use 1 / sqrt(d_head)).  stream
+ * is a hipStream_t (NULL: the default stream).  workspace may be NULL when
+ * gqa_decode_workspace_size() is 0.  num_seqs == 0 returns GQA_OK and
+ * launches nothing.
+ */
+gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_table, const int32_t* ctx_lens, void* out,
+                        int num_seqs, int max_blocks_per_seq, int h_q, int h_kv,
+                        int d_head, int block_size, float scale, gqa_dtype_t dtype,
+                        void* workspace, size_t workspace_bytes,
+                        const gqa_policy_t* policy, void* stream);
+
+/*
+ * Contiguous decode: every sequence holds s_kv tokens (s_kv >= 0) in a
+ * [num_seqs, s_kv, h_kv, d_head] cache; with s_kv == 0 the output is zero and
+ * k, v may be NULL.  Same rules as gqa_decode otherwise.
+ */
+gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, void* out,
+                                   int num_seqs, int s_kv, int h_q, int h_kv, int d_head,
+                                   float scale, gqa_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes,
+                                   const gqa_policy_t* policy, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* gqa_status_string(gqa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle.
+
+Tolerances are those in tests/parity.py.  Small cases are compared element by
+element over every output; the five named workloads at full size are compared
+on sampled (sequence, query head) rows the oracle computes one by one, in the
+launch configuration the bench times (default policy) and under the pages'
+policy (partition 512, single pass up to 8192).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import reference as R
+from tests.parity import assert_close, bits_to_device, case_to_device, run_case
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import decode_attention_08_amd as m
+    return m
+
+
+def _policies(gq):
+    return {
+        "default": None,
+        "pages": gq.policy_pages(),
+        "all_split_p32": gq.policy_pages(partition_size=32, v1_max_ctx=0),
+        "all_split_p96": gq.policy_pages(partition_size=96, v1_max_ctx=0),
+        "all_single": gq.policy_pages(v1_max_ctx=1 << 30),
+    }
+
+
+EDGE_LENGTHS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 511, 512, 513, 1000, 8192, 8193]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_edge_lengths_all_policies(gq, dtype, d):
+    case = W.paged_case(f"edges_{dtype}_{d}", 100 + d, EDGE_LENGTHS, h_q=16, h_kv=2, d=d,
+                        dtype=dtype, extra_blocks=3)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name, pol in _policies(gq).items():
+        print(f"edges dtype={dtype} d={d} policy={name}", flush=True)
+        got = run_case(dev, policy=pol)
+        assert_close(got, ref, dtype, what=f"edges {dtype} d={d} {name}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
+def test_group_sizes(gq, G):
+    h_kv = 2
+    case = W.paged_case(f"group{G}", 200 + G, [700, 33, 1], h_q=G * h_kv, h_kv=h_kv, d=128,
+                        dtype=W.F16)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name in ("default", "all_split_p96"):
+        got = run_case(dev, policy=_policies(gq)[name])
+        assert_close(got, ref, W.F16, what=f"G={G} {name}")
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+def test_block_sizes(gq, bs):
+    case = W.paged_case(f"bs{bs}", 300 + bs, [1, bs - 1, bs, bs + 1, 3 * bs + 5, 700],
+                        h_q=8, h_kv=1, d=64, dtype=W.BF16, block_size=bs, extra_blocks=1)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name in ("default", "pages", "all_split_p32"):
+        got = run_case(dev, policy=_policies(gq)[name])
+        assert_close(got, ref, W.BF16, what=f"bs={bs} {name}")
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+def test_contiguous_small(gq, dtype):
+    case = W.contiguous_case(f"contig_{dtype}", 400, 3, 32, 8, 128, 1000, dtype)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name, pol in _policies(gq).items():
+        got = run_case(dev, policy=pol)
+        assert_close(got, ref, dtype, what=f"contig {dtype} {name}")
+
+
+def test_zero_length_gives_zeros(gq):
+    case = W.paged_case("zeros", 500, [0, 5, 0, 40], h_q=8, h_kv=2, d=128, dtype=W.F16)
+    dev = case_to_device(case, DEV)
+    ref = R.decode(case)
+    for name, pol in _policies(gq).items():
+        got = run_case(dev, policy=pol)
+        assert np.array_equal(got[0], np.zeros((8, 128))) and np.array_equal(got[2], got[0]), name
+        assert_close(got, ref, W.F16, what=f"zeros {name}")
+    c0 = W.contiguous_case("s0", 501, 2, 4, 1, 64, 0)
+    got = run_case(case_to_device(c0, DEV))
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_single_token_is_exact(gq):
+    """S_kv = 1: the output is v_0 bit for bit (p = 1, l = 1)."""
+    for dtype in (W.F16, W.BF16):
+        case = W.contiguous_case("s1", 600, 4, 16, 4, 128, 1, dtype)
+        got = run_case(case_to_device(case, DEV))
+        want = R.upcast(case.v[:, 0], dtype)                      # [B, h_kv, d]
+        want = np.repeat(want, 4, axis=1)                          # query head i -> kv i // 4
+        assert np.array_equal(got, want), dtype
+
+
+def test_zero_query_is_mean(gq):
+    case = W.contiguous_case("q0", 700, 2, 8, 2, 64, 777, W.F16)
+    case.q[:] = 0
+    got = run_case(case_to_device(case, DEV))
+    Vf = R.upcast(case.v, case.dtype)                              # [B, S, h_kv, d]
+    want = np.repeat(Vf.mean(axis=1), 4, axis=1)
+    assert_close(got, want, W.F16, what="q=0 mean")
+
+
+def test_large_logits_stable(gq):
+    case = W.paged_case("big", 800, [300, 2000], h_q=8, h_kv=1, d=128, dtype=W.BF16, scale=25.0)
+    ref = R.decode(case)
+    for name, pol in _policies(gq).items():
+        got = run_case(case_to_device(case, DEV), policy=pol)
+        assert_close(got, ref, W.BF16, what=f"large logits {name}")
+
+
+def test_paged_bitwise_equals_contiguous(gq):
+    """A random block table and the contiguous layout of the same tokens agree bit
+    for bit (same partitions, same reduction order)."""
+    S = 1500
+    paged = W.paged_case("pc", 900, [S] * 3, h_q=16, h_kv=2, d=128, dtype=W.F16, extra_blocks=2)
+    k = np.zeros((3, S, 2, 128), np.uint16)
+    v = np.zeros_like(k)
+    for s in range(3):
+        for t in range(S):
+            b = paged.block_table[s, t // 16]
+            k[s, t] = paged.k[b, t % 16]
+            v[s, t] = paged.v[b, t % 16]
+    contig = W.DecodeCase("c", W.F16, "contiguous", paged.q, k, v, paged.ctx_lens, None,
+                          16, 2, 128, paged.scale, s_kv=S)
+    for name, pol in _policies(gq).items():
+        a = run_case(case_to_device(paged, DEV), policy=pol)
+        b = run_case(case_to_device(contig, DEV), policy=pol)
+        assert np.array_equal(a, b), name
+
+
+def test_deterministic(gq):
+    case = W.workload("paged_b64")
+    dev = case_to_device(case, DEV)
+    a = run_case(dev, policy=gq.policy_pages(v1_max_ctx=0))
+    for _ in range(2):
+        assert np.array_equal(a, run_case(dev, policy=gq.policy_pages(v1_max_ctx=0)))
+
+
+def test_phases_split_equals_whole(gq):
+    case = W.paged_case("ph", 1000, [5000, 100, 9000], h_q=32, h_kv=4, d=128, dtype=W.F16)
+    dev = case_to_device(case, DEV)
+    pol = gq.policy_pages()
+    whole = run_case(dev, policy=pol)
+    ws = torch.empty(gq.workspace_size(3, 32, 128, case.max_blocks * 16, pol),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(dev["q"])
+    run_case(dev, policy=gq.policy_pages(phases=1), out=out, workspace=ws)
+    got = run_case(dev, policy=gq.policy_pages(phases=2), out=out, workspace=ws)
+    assert np.array_equal(whole, got)
+
+
+def _sample_heads(case, rng, n_seq, per_seq):
+    seqs = sorted(set([0, case.num_seqs - 1] +
+                      rng.choice(case.num_seqs, size=min(n_seq, case.num_seqs), replace=False).tolist()))
+    if case.layout == "paged":                  # always include the longest sequence
+        seqs = sorted(set(seqs + [int(np.argmax(case.ctx_lens))]))
+    heads = []
+    for s in seqs:
+        idx = sorted(set([0, case.h_q - 1] + rng.choice(case.h_q, size=per_seq, replace=False).tolist()))
+        heads += [(s, i) for i in idx]
+    return heads
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_named_workloads_sampled(gq, name):
+    case = W.workload(name)
+    rng = np.random.default_rng(12345)
+    heads = ([(s, i) for s in range(case.num_seqs) for i in range(case.h_q)]
+             if case.kv_bytes <= (1 << 27) else _sample_heads(case, rng, 6, 6))
+    ref = R.decode(case, heads=heads)
+    dev = case_to_device(case, DEV)
+    for pname in ("default", "pages"):
+        print(f"workload {name} policy={pname} rows={len(heads)}", flush=True)
+        got = run_case(dev, policy=_policies(gq)[pname])
+        assert np.all(np.isfinite(got)), pname
+        assert_close(got, ref, case.dtype, what=f"{name} {pname}")
