@@ -1,0 +1,296 @@
+"""Benchmark: single-query GQA decode attention on one MI355X.
+
+One step = one pass of the whole decode path (partition kernel + merge kernel)
+over one batch of synthetic inputs already resident in HBM.  K/V are cycled
+over enough device copies (>= 1 GiB in total, i.e. more than four times the
+256 MB Infinity Cache) that no step can be served from the cache a previous
+step filled.
+
+Prints ONE JSON line.  `value` is K+V GB/s of the headline workload
+(algorithmic K+V bytes / wall time per step between synchronisations);
+`roofline` gives the partition kernel's own HBM roofline fraction, timed with
+HIP events on the launch stream inside the timed region; `cpu_baseline` times
+the float64 oracle on a bounded sample of the same workload; `also` carries
+the other full-size workloads.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload contig_b8]
+  python bench.py --summarize-rocprof DIR     # rocprofv3 csv -> short text
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "K/V HBM GB/s (and % of peak) + decode attention µs/step, 1 GPU"
+PEAK_GBS = 8000.0                       # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30                  # K/V bytes cycled per step sequence
+HEADLINE = "contig_b8"
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_08_amd", "csrc", "gqa_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ timing --
+
+def time_workload(case, policy_name: str, steps: int, warmup: int, with_events: bool = True):
+    """Time `steps` decode steps of one workload; returns a dict of figures."""
+    import torch
+    import decode_attention_08_amd as gq
+    from tests.parity import bits_to_device
+
+    dev = torch.device("cuda:0")
+    pol = gq.policy_default() if policy_name == "default" else gq.policy_pages()
+    q = bits_to_device(case.q, case.dtype, dev)
+    k0 = bits_to_device(case.k, case.dtype, dev)
+    v0 = bits_to_device(case.v, case.dtype, dev)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    copies = max(2, math.ceil(ROTATE_BYTES / max(1, pool_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    if case.layout == "paged":
+        bt = torch.from_numpy(case.block_table).to(dev)
+        ctx = torch.from_numpy(case.ctx_lens).to(dev)
+        call = gq.prepare(q, k0, v0, block_table=bt, ctx_lens=ctx, scale=case.scale, policy=pol)
+    else:
+        call = gq.prepare(q, k0, v0, scale=case.scale, policy=pol)
+    has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.d,
+                                  (case.max_blocks * case.block_size if case.layout == "paged"
+                                   else case.s_kv), pol) > 0
+
+    def step(i, ev=None):
+        k, v = ks[i % copies], vs[i % copies]
+        if ev is None:
+            call(k, v, phases=3)
+            return
+        ev[0].record()
+        call(k, v, phases=1)
+        ev[1].record()
+        if has_merge:
+            call(k, v, phases=2)
+        ev[2].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, evs[i] if with_events else None)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    res = {"workload": case.name, "policy": policy_name,
+           "partition_size": pol.partition_size, "v1_max_ctx": pol.v1_max_ctx,
+           "kv_bytes": case.kv_bytes, "copies": copies,
+           "ms_per_step": wall * 1e3, "us_per_step": wall * 1e6,
+           "gbs": case.kv_bytes / wall / 1e9}
+    res["pct_of_peak"] = 100.0 * res["gbs"] / PEAK_GBS
+    if with_events:
+        part = sorted(e[0].elapsed_time(e[1]) for e in evs)      # ms
+        merge = sorted(e[1].elapsed_time(e[2]) for e in evs)
+        step_ev = sorted(e[0].elapsed_time(e[2]) for e in evs)
+        mean_part = sum(part) / len(part)
+        res.update({
+            "partition_us_mean": mean_part * 1e3,
+            "partition_us_median": part[len(part) // 2] * 1e3,
+            "merge_us_mean": sum(merge) / len(merge) * 1e3,
+            "step_us_events_median": step_ev[len(step_ev) // 2] * 1e3,
+            "step_us_events_p10": step_ev[len(step_ev) // 10] * 1e3,
+            "step_us_events_p90": step_ev[(9 * len(step_ev)) // 10] * 1e3,
+            "partition_gbs": case.kv_bytes / (mean_part * 1e-3) / 1e9,
+        })
+    del ks, vs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The float64 oracle, as it stands, on whole (sequence, KV head) slices of the
+    workload, one BLAS thread; repeated over slices until about budget_s."""
+    from threadpoolctl import threadpool_limits
+    import numpy as np
+    from oracle import reference as R
+
+    G = case.h_q // case.h_kv
+    pairs = [(s, j) for s in range(case.num_seqs) for j in range(case.h_kv)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(pairs))
+    done_bytes, done_pairs, t_used = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        for n in order:
+            s, j = pairs[n]
+            heads = [(s, j * G + g) for g in range(G)]
+            t0 = time.perf_counter()
+            R.decode(case, heads=heads)
+            t_used += time.perf_counter() - t0
+            done_bytes += int(case.ctx_lens[s]) * case.d * 2 * 2
+            done_pairs += 1
+            if t_used >= budget_s:
+                break
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done_pairs} of {len(pairs)} (sequence, KV head) slices of {case.name}, "
+                       f"{done_bytes} K/V bytes in {t_used:.2f} s, float64 numpy, 1 BLAS thread"),
+            "seconds": t_used}
+
+
+def traffic_for(workload: str, policy: str, kv_bytes: int):
+    """Measured HBM bytes per partition-kernel launch, if the counters were taken
+    on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(f"{workload}/{policy}")
+    if not rec or rec.get("source_sha") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- rocprof --
+
+def summarize_rocprof(path: str) -> str:
+    """Condense rocprofv3 --stats / --pmc csv files under `path` into short text."""
+    import csv
+    lines = []
+    for fn in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append(f"# kernel stats: {os.path.relpath(fn, path)}")
+        with open(fn) as f:
+            rows = list(csv.DictReader(f))
+        for r in rows:
+            name = r.get("Name", "")
+            short = name.split("(")[0][:90]
+            lines.append(f"{short:90s} calls={r.get('Calls')} avg_ns={float(r.get('AverageNs', 0)):.0f} "
+                         f"min_ns={r.get('MinNs')} max_ns={r.get('MaxNs')} pct={float(r.get('Percentage', 0)):.2f}")
+    for fn in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        lines.append(f"# counters: {os.path.relpath(fn, path)}")
+        agg = {}
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", "").split("(")[0][:90]
+                key = (name, r.get("Counter_Name"))
+                a = agg.setdefault(key, [0.0, 0])
+                a[0] += float(r.get("Counter_Value", 0))
+                a[1] += 1
+        # counter rows come per dispatch (possibly per XCD/instance); report the per-dispatch sum
+        disp = {}
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", "").split("(")[0][:90]
+                key = (name, r.get("Counter_Name"))
+                disp.setdefault(key, set()).add(r.get("Dispatch_Id"))
+        for (name, cn), (tot, n) in sorted(agg.items()):
+            nd = len(disp[(name, cn)])
+            lines.append(f"{name:90s} {cn}={tot / max(1, nd):.1f} per dispatch ({nd} dispatches)")
+    return "\n".join(lines)
+
+
+# ------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--policy", default="default", choices=["default", "pages"])
+    ap.add_argument("--no-also", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run one torch copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    case = W.workload(args.workload)
+    head = time_workload(case, args.policy, args.steps, args.warmup)
+    print(f"[bench] {case.name}/{args.policy}: {head['us_per_step']:.1f} us/step wall, "
+          f"{head['gbs']:.0f} GB/s, partition {head['partition_us_mean']:.1f} us", file=sys.stderr,
+          flush=True)
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    also = {}
+    if not args.no_also:
+        for name in W.WORKLOADS:
+            c = case if name == args.workload else W.workload(name)
+            for pol in ("default", "pages"):
+                if name == args.workload and pol == args.policy:
+                    continue
+                r = time_workload(c, pol, args.steps, args.warmup)
+                also[f"{name}/{pol}"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                         for k, v in r.items() if k not in ("workload", "policy")}
+                print(f"[bench] {name}/{pol}: {r['us_per_step']:.1f} us/step wall, {r['gbs']:.0f} GB/s, "
+                      f"partition {r['partition_us_mean']:.1f} us ({r['partition_gbs']:.0f} GB/s)",
+                      file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu else cpu_baseline(case)
+    achieved = head["partition_gbs"]
+    traffic = traffic_for(case.name, args.policy, case.kv_bytes)
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
+        "config": {"workload": case.name, "desc": W.WORKLOADS[case.name][1],
+                   "policy": args.policy, "partition_size": head["partition_size"],
+                   "v1_max_ctx": head["v1_max_ctx"], "kv_bytes": case.kv_bytes,
+                   "kv_copies_rotated": head["copies"]},
+        "us_per_step": round(head["us_per_step"], 2),
+        "pct_of_peak": round(head["pct_of_peak"], 2),
+        "step_us_events": {"median": round(head["step_us_events_median"], 2),
+                           "p10": round(head["step_us_events_p10"], 2),
+                           "p90": round(head["step_us_events_p90"], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "partition_kernel",
+                     "kernel_us_mean": round(head["partition_us_mean"], 3),
+                     "merge_us_mean": round(head["merge_us_mean"], 3)},
+        "cpu_baseline": cpu,
+        "also": also,
+        "kernel_source_sha": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

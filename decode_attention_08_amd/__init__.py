@@ -19,4 +19,6 @@ from ._binding import (  # noqa: F401
     status_string,
     workspace_size,
     EXPORTED_SYMBOLS,
+    PreparedCall,
+    prepare,
 )

@@ -179,3 +179,65 @@ def decode_contiguous(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     if st != 0:
         raise GqaError(st)
     return out
+
+
+class PreparedCall:
+    """A decode call with its arguments marshalled once, for tight loops.
+
+    ``call(k=None, v=None, phases=None)`` invokes the C entry point again with
+    the same buffers, optionally another K/V pair of identical shape and
+    dtype, and optionally a different ``phases`` value.  The caller keeps
+    every tensor alive.
+    """
+
+    def __init__(self, fn, args, k_index, policy: Policy, keep):
+        self._fn = fn
+        self._args = list(args)
+        self._k_index = k_index
+        self._policy = Policy(policy.partition_size, policy.v1_max_ctx, policy.phases, 0)
+        self._pol_index = len(args) - 2
+        self._args[self._pol_index] = ctypes.byref(self._policy)
+        self._keep = keep
+
+    def __call__(self, k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                 phases: Optional[int] = None) -> None:
+        args = self._args
+        if k is not None:
+            args = list(args)
+            args[self._k_index] = k.data_ptr()
+            args[self._k_index + 1] = v.data_ptr()
+        if phases is not None:
+            self._policy.phases = phases
+        st = self._fn(*args)
+        if st != 0:
+            raise GqaError(st)
+
+
+def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
+            workspace=None, policy: Optional[Policy] = None, stream=None) -> PreparedCall:
+    """Validate once (same checks as decode / decode_contiguous) and return a
+    PreparedCall.  Paged when block_table is given, contiguous otherwise."""
+    policy = policy_default() if policy is None else policy
+    if block_table is not None:
+        out = _common(q, {"q": q, "k_cache": k, "v_cache": v, "block_table": block_table,
+                          "ctx_lens": ctx_lens}, out)
+        B, h_q, d = q.shape
+        _, bs, h_kv, _ = k.shape
+        max_blocks = block_table.shape[1]
+        need = workspace_size(B, h_q, d, max_blocks * bs, policy)
+        workspace, ws_bytes = _workspace(workspace, need, q.device)
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(ctx_lens), _ptr(out), B,
+                max_blocks, h_q, h_kv, d, bs, scale, _dtype_code(q), _ptr(workspace), ws_bytes,
+                None, _stream(stream, q.device))
+        return PreparedCall(lib.gqa_decode, args, 1, policy,
+                            (q, k, v, block_table, ctx_lens, out, workspace))
+    out = _common(q, {"q": q, "k": k, "v": v}, out)
+    B, h_q, d = q.shape
+    _, S, h_kv, _ = k.shape
+    need = workspace_size(B, h_q, d, S, policy)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, h_q, h_kv, d, scale, _dtype_code(q),
+            _ptr(workspace), ws_bytes, None, _stream(stream, q.device))
+    return PreparedCall(lib.gqa_decode_contiguous, args, 1, policy, (q, k, v, out, workspace))
