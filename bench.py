@@ -162,40 +162,61 @@ def traffic_for(workload: str, policy: str, kv_bytes: int):
 
 # ---------------------------------------------------------------- rocprof --
 
-def summarize_rocprof(path: str) -> str:
-    """Condense rocprofv3 --stats / --pmc csv files under `path` into short text."""
-    import csv
-    lines = []
-    for fn in sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)):
-        lines.append(f"# kernel stats: {os.path.relpath(fn, path)}")
-        with open(fn) as f:
-            rows = list(csv.DictReader(f))
-        for r in rows:
-            name = r.get("Name", "")
-            short = name.split("(")[0][:90]
-            lines.append(f"{short:90s} calls={r.get('Calls')} avg_ns={float(r.get('AverageNs', 0)):.0f} "
-                         f"min_ns={r.get('MinNs')} max_ns={r.get('MaxNs')} pct={float(r.get('Percentage', 0)):.2f}")
-    for fn in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
-        lines.append(f"# counters: {os.path.relpath(fn, path)}")
-        agg = {}
-        with open(fn) as f:
-            for r in csv.DictReader(f):
-                name = r.get("Kernel_Name", "").split("(")[0][:90]
-                key = (name, r.get("Counter_Name"))
-                a = agg.setdefault(key, [0.0, 0])
-                a[0] += float(r.get("Counter_Value", 0))
-                a[1] += 1
-        # counter rows come per dispatch (possibly per XCD/instance); report the per-dispatch sum
-        disp = {}
-        with open(fn) as f:
-            for r in csv.DictReader(f):
-                name = r.get("Kernel_Name", "").split("(")[0][:90]
-                key = (name, r.get("Counter_Name"))
-                disp.setdefault(key, set()).add(r.get("Dispatch_Id"))
-        for (name, cn), (tot, n) in sorted(agg.items()):
-            nd = len(disp[(name, cn)])
-            lines.append(f"{name:90s} {cn}={tot / max(1, nd):.1f} per dispatch ({nd} dispatches)")
-    return "\n".join(lines)
+def _rocpd(path: str, pattern: str):
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, pattern, "*_results.db"), recursive=True))
+    return [(db, sqlite3.connect(db)) for db in dbs]
+
+
+def _short(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").split("(Params)")[0][:100]
+
+
+def summarize_rocprof(path: str, probe_bytes: int = 1 << 30):
+    """Condense the rocprofv3 databases of one profiled bench run.
+
+    Expects `path`/trace (--kernel-trace --stats), `path`/fetch (--pmc
+    FETCH_SIZE) and `path`/write (--pmc WRITE_SIZE), each made with
+    --copy-probe 1024 for the counter runs.  Counter values (KiB per dispatch)
+    are scaled by what the same counter reads for the 1 GiB probe copy (the
+    largest copy dispatch of the run).  Returns (text, traffic record).
+    """
+    lines, rec = [], {}
+    for db, con in _rocpd(path, "trace"):
+        lines.append(f"# kernel trace: {os.path.relpath(db, path)}")
+        rows = con.execute(
+            "select name, count(*), avg(duration), min(duration), max(duration), grid_x, "
+            "workgroup_x, vgpr_count, accum_vgpr_count, lds_size from kernels group by name "
+            "order by sum(duration) desc").fetchall()
+        for n, c, avg, mn, mx, gx, wx, vg, ag, lds in rows:
+            lines.append(f"{_short(n):100s} calls={c} avg_ns={avg:.0f} min_ns={mn} max_ns={mx} "
+                         f"grid={gx} wg={wx} vgpr={vg} agpr={ag} lds={lds}")
+            if "partition_kernel" in n:
+                rec["partition_avg_ns"] = avg
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        sub = "fetch" if counter == "FETCH_SIZE" else "write"
+        for db, con in _rocpd(path, sub):
+            lines.append(f"# counter {counter}: {os.path.relpath(db, path)}")
+            rows = con.execute(
+                "select kernel_name, dispatch_id, sum(value) from counters_collection "
+                "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+            per = {}
+            for n, _, v in rows:
+                per.setdefault(_short(n), []).append(v)
+            probe = max((v for n, vs in per.items() if "copyBuffer" in n for v in vs), default=None)
+            factor = probe_bytes / (probe * 1024.0) if probe else None
+            for n, vs in sorted(per.items()):
+                lines.append(f"{n:100s} {counter}_KiB avg={sum(vs) / len(vs):.1f} "
+                             f"min={min(vs):.1f} max={max(vs):.1f} dispatches={len(vs)}")
+            lines.append(f"calibration: 1 GiB probe copy reads {probe} KiB -> factor {factor}")
+            part = [v for n, vs in per.items() if "partition_kernel" in n for v in vs]
+            if part and factor:
+                rec[counter] = {"kib_avg": sum(part) / len(part), "factor": factor,
+                                "bytes_per_launch": sum(part) / len(part) * 1024.0 * factor}
+    if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
+        rec["bytes_per_launch"] = rec["FETCH_SIZE"]["bytes_per_launch"] + rec["WRITE_SIZE"]["bytes_per_launch"]
+    rec["source_sha"] = source_hash()
+    return "\n".join(lines), rec
 
 
 # ------------------------------------------------------------------- main --
@@ -212,10 +233,23 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run one torch copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--record-traffic", metavar="WORKLOAD/POLICY",
+                    help="with --summarize-rocprof: store the traffic record in profiles/traffic.json")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
-        print(summarize_rocprof(args.summarize_rocprof))
+        text, rec = summarize_rocprof(args.summarize_rocprof)
+        print(text)
+        print("# traffic record: " + json.dumps(rec))
+        if args.record_traffic:
+            try:
+                with open(TRAFFIC_FILE) as f:
+                    table = json.load(f)
+            except (OSError, ValueError):
+                table = {}
+            table[args.record_traffic] = rec
+            with open(TRAFFIC_FILE, "w") as f:
+                json.dump(table, f, indent=1, sort_keys=True)
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
