@@ -66,7 +66,7 @@ def time_workload(case, policy_name: str, steps: int, warmup: int, with_events: 
         call = gq.prepare(q, k0, v0, block_table=bt, ctx_lens=ctx, scale=case.scale, policy=pol)
     else:
         call = gq.prepare(q, k0, v0, scale=case.scale, policy=pol)
-    has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.d,
+    has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.h_kv, case.d,
                                   (case.max_blocks * case.block_size if case.layout == "paged"
                                    else case.s_kv), pol) > 0
 

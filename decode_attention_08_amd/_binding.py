@@ -39,7 +39,7 @@ lib.gqa_policy_default.argtypes = [ctypes.POINTER(Policy)]
 lib.gqa_policy_default.restype = None
 lib.gqa_policy_pages.argtypes = [ctypes.POINTER(Policy)]
 lib.gqa_policy_pages.restype = None
-lib.gqa_decode_workspace_size.argtypes = [_I, _I, _I, _I, ctypes.POINTER(Policy)]
+lib.gqa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(Policy)]
 lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
 lib.gqa_decode.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                            _P, ctypes.c_size_t, ctypes.POINTER(Policy), _P]
@@ -81,9 +81,9 @@ def _pref(policy: Optional[Policy]):
     return None if policy is None else ctypes.byref(policy)
 
 
-def workspace_size(num_seqs: int, h_q: int, d_head: int, max_ctx: int,
+def workspace_size(num_seqs: int, h_q: int, h_kv: int, d_head: int, max_ctx: int,
                    policy: Optional[Policy] = None) -> int:
-    return int(lib.gqa_decode_workspace_size(num_seqs, h_q, d_head, max_ctx, _pref(policy)))
+    return int(lib.gqa_decode_workspace_size(num_seqs, h_q, h_kv, d_head, max_ctx, _pref(policy)))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -149,7 +149,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _require(block_table.shape[0] == B and ctx_lens.shape[0] == B, "batch sizes differ")
     max_blocks = block_table.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = workspace_size(B, h_q, d, max_blocks * bs, policy)
+    need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     st = lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
                         _ptr(out), B, max_blocks, h_q, h_kv, d, bs, scale, _dtype_code(q),
@@ -171,7 +171,7 @@ def decode_contiguous(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     Bk, S, h_kv, dk = k.shape
     _require(Bk == B and dk == d, "k/v shape does not match q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = workspace_size(B, h_q, d, S, policy)
+    need = workspace_size(B, h_q, h_kv, d, S, policy)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     st = lib.gqa_decode_contiguous(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, h_q, h_kv, d,
                                    scale, _dtype_code(q), _ptr(workspace), ws_bytes,
@@ -224,7 +224,7 @@ def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
         B, h_q, d = q.shape
         _, bs, h_kv, _ = k.shape
         max_blocks = block_table.shape[1]
-        need = workspace_size(B, h_q, d, max_blocks * bs, policy)
+        need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
         workspace, ws_bytes = _workspace(workspace, need, q.device)
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(ctx_lens), _ptr(out), B,
@@ -235,7 +235,7 @@ def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
     out = _common(q, {"q": q, "k": k, "v": v}, out)
     B, h_q, d = q.shape
     _, S, h_kv, _ = k.shape
-    need = workspace_size(B, h_q, d, S, policy)
+    need = workspace_size(B, h_q, h_kv, d, S, policy)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, h_q, h_kv, d, scale, _dtype_code(q),

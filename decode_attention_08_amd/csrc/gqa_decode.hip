@@ -1,18 +1,23 @@
 // Single-query GQA decode attention for MI355X (gfx950, CDNA4).
 //
-// Two kernels:
-//   partition_kernel  one workgroup per (partition, KV head, sequence).  Its
-//                     NW waves stream 32-token tiles of K and V from HBM and
-//                     keep a running (m, l, O) for all G query heads sharing
-//                     the KV head (decode-long page, "Local attention" tile
-//                     sweep and "_merge_running").  At the end the waves are
-//                     merged in LDS; a single-partition sequence is
-//                     normalised and stored (kernel-map page,
-//                     "paged_attention_v1"), a split one writes its fp32
-//                     partial triple (kernel-map page, "paged_attention_v2").
-//   merge_kernel      one wave per (sequence, query head) of a split sequence:
-//                     the n-ary form of "_merge_running" followed by the
-//                     decode-long page's "Final normalise + store".
+// Kernels:
+//   partition kernels  a workgroup holds one wave per KV head of a head group
+//                      (HPW heads, up to 8); all its waves walk the same token
+//                      segment of one sequence, so that together they read
+//                      whole K/V rows (the cache interleaves the KV heads of
+//                      a token).  Each wave computes, for its KV head, the
+//                      partial triple (m, l, O) of the G query heads sharing
+//                      it (decode-long page, "Local attention" tile sweep and
+//                      "_merge_running") and either stores the normalised
+//                      output (the segment is the whole sequence; kernel-map
+//                      page, "paged_attention_v1") or the fp32 partial
+//                      (kernel-map page, "paged_attention_v2").  Two
+//                      schedulers feed them: fixed partitions (one workgroup
+//                      each) and a balanced persistent grid.
+//   merge kernels      one wave per (sequence, query head) of a split
+//                      sequence: the n-ary form of "_merge_running" over the
+//                      partials, then the decode-long page's "Final
+//                      normalise + store".
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{f16,bf16}, wave64).  The G <= 16
 // query heads of one KV head are the 16-wide N side of both products, padded
@@ -25,12 +30,16 @@
 // the four 16-lane groups.  K feeds the A operand straight from HBM with
 // 16-byte loads (8 consecutive d of one token per lane).  V needs tokens
 // along the operand's K side, so each wave stages its V tile in LDS with
-// coalesced 16-byte stores and reads it back transposed.
+// coalesced 16-byte stores and reads it back transposed.  Every wave keeps
+// the next tile's K and V loads in flight while it computes the current one.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <algorithm>
+#include <mutex>
 
 #include "gqa_decode.h"
 
@@ -41,9 +50,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 32;        // tokens per wave iteration (two 16-token MFMA row blocks)
-constexpr int kWaves = 4;        // waves per partition workgroup
-constexpr int kRedStride = 20;   // floats per (wave, d) row of the cross-wave buffer
+constexpr int kTile = 32;            // tokens per wave iteration (two 16-token MFMA row blocks)
+constexpr int kMaxHeadsPerGroup = 8; // waves (KV heads) per partition workgroup, at most
+constexpr int kMaxGrid = 2048;       // persistent grid cap (two partial slots per workgroup)
+constexpr int kMinChunkTiles = 2;    // smallest balanced share: 2 tiles = 64 tokens
+constexpr int kMaxSeqsBalanced = 8192;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- dtypes --
@@ -84,36 +95,52 @@ struct Params {
   uint16_t* out;
   const int32_t* block_table;   // paged only
   const int32_t* ctx_lens;      // paged only
-  float2* part_ml;              // [num_seqs, h_q, max_parts] (m in log2 units, l)
-  float* part_o;                // [num_seqs, h_q, max_parts, d]
+  float2* part_ml;              // partial (m in log2 units, l) per (slot, query head)
+  float* part_o;                // partial un-normalised O row per (slot, query head)
+  int4* desc;                   // balanced mode: per (sequence, head group) segment record
   int num_seqs;
   int h_q;
   int h_kv;
   int group;                    // G = h_q / h_kv
+  int hpw;                      // KV heads (waves) per workgroup
+  int n_groups;                 // h_kv / hpw
   int s_kv;                     // contiguous length
   int max_blocks;               // paged table width
   int bs_shift;                 // log2(block_size)
   int max_ctx;                  // clamp for ctx_lens
-  int part_size;
-  int v1_max_ctx;
-  int max_parts;
+  int part_size;                // fixed mode: tokens per partition
+  int v1_max_ctx;               // sequences this short are never split
+  int max_parts;                // fixed mode: partition slots per (sequence, query head)
   float c;                      // scale * log2(e)
 };
+
+// Read-only tables (block table, context lengths) are read through the
+// constant address space: they are not written while a kernel runs, and a
+// wave-uniform index then becomes a scalar load instead of a vector load that
+// would share the vector-memory counter with the K/V stream.
+template <class T>
+__device__ __forceinline__ T load_const(const T* p, int64_t i) {
+  typedef const __attribute__((address_space(4))) T* const_ptr;
+  return ((const_ptr)p)[i];
+}
 
 template <bool PAGED>
 __device__ __forceinline__ int seq_len(const Params& a, int s) {
   if constexpr (PAGED) {
-    const int L = a.ctx_lens[s];
+    const int L = load_const(a.ctx_lens, s);
     return min(max(L, 0), a.max_ctx);
   } else {
     return a.s_kv;
   }
 }
 
+// tiles of 32 tokens a sequence occupies in the balanced work space (an empty
+// sequence still occupies one, so that exactly one workgroup writes its zero row)
+__device__ __forceinline__ int seq_tiles(int L) { return max(1, (L + kTile - 1) / kTile); }
+
 // Orders this wave's LDS stores before its later LDS loads (and vice versa):
 // the asm is a compiler memory barrier and the wait retires the wave's
-// outstanding LDS operations.  Each wave only touches its own LDS region, so
-// no workgroup barrier is needed inside the token loop.
+// outstanding LDS operations.  Each wave only touches its own LDS tile.
 __device__ __forceinline__ void wave_lds_fence() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
@@ -124,36 +151,43 @@ __device__ __forceinline__ int slot_token(int grp, int e) {
   return (e & 4) * 4 + grp * 4 + (e & 3);
 }
 
-// ------------------------------------------------------ partition kernel --
+// Staged V tiles are row-major without padding; the 16-byte chunks of a row
+// are XOR-permuted so that the transposed reads of the four lane groups
+// (rows 4 grp + e) fall in distinct LDS banks.
+__device__ __forceinline__ int v_swizzle(int row) { return 2 * ((row >> 2) & 3); }
 
-template <class DT, int D, bool PAGED, int NW>
-__global__ __launch_bounds__(NW * 64) void partition_kernel(Params a) {
-  constexpr int KK = D / 32;        // MFMA steps over d for Q.K^T
-  constexpr int NB = D / 16;        // 16-row blocks of O^T
-  constexpr int VS = D + 8;         // uint16 per staged V row (pad spreads LDS banks)
-  constexpr int CH = D / 8;         // 16-byte chunks per K/V row
-  constexpr int RPI = 64 / CH;      // V rows per 16-byte load instruction
-  constexpr int NIT = kTile / RPI;  // V load instructions per tile
-  constexpr int V_LDS = NW * kTile * VS * 2;
-  constexpr int RED_LDS = NW * D * kRedStride * 4;
-  constexpr int LDS_BYTES = V_LDS > RED_LDS ? V_LDS : RED_LDS;
-  static_assert(LDS_BYTES <= 64 * 1024, "workgroup LDS budget");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+template <int D>
+struct Geo {
+  static constexpr int KK = D / 32;        // MFMA steps over d for Q.K^T
+  static constexpr int NB = D / 16;        // 16-row blocks of O^T
+  static constexpr int CH = D / 8;         // 16-byte chunks per K/V row
+  static constexpr int RPI = 64 / CH;      // V rows per 16-byte load instruction
+  static constexpr int NIT = kTile / RPI;  // V load instructions per tile
+  static constexpr int V_TILE = kTile * D; // uint16 per staged V tile (one per wave)
+};
 
-  // ---- work item: blockIdx.x = (s * h_kv + j) * max_parts + p
-  const int p = blockIdx.x % a.max_parts;
-  const int sj = blockIdx.x / a.max_parts;
-  const int j = sj % a.h_kv;
-  const int s = sj / a.h_kv;
-  const int L = seq_len<PAGED>(a, s);
-  const bool split = L > a.v1_max_ctx;
-  const int n_part = split ? (L + a.part_size - 1) / a.part_size : 1;
-  if (p >= n_part) return;                       // uniform over the workgroup
-  const int t0 = split ? p * a.part_size : 0;
-  const int t1 = split ? min(t0 + a.part_size, L) : L;
+// ------------------------------------------------- one wave, one segment --
+//
+// One wave computes the partial triple of tokens [t0, t1) of (sequence s,
+// KV head j) for the G query heads of that KV head and either stores the
+// normalised output (complete == true: the segment is the whole sequence) or
+// the fp32 partial at pml[g * ml_stride], po[g * o_stride] for head g.  The
+// wave walks its 32-token tiles in order and keeps the next tile's K and V
+// loads in flight while it computes the current one.  vt is the wave's LDS
+// tile.
 
+template <class DT, int D, bool PAGED>
+__device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int s, int j, int t0,
+                                             int t1, bool complete, float2* pml,
+                                             int64_t ml_stride, float* po, int64_t o_stride) {
+  using Gm = Geo<D>;
+  constexpr int KK = Gm::KK, NB = Gm::NB, CH = Gm::CH, RPI = Gm::RPI, NIT = Gm::NIT;
+  // uniform over the wave; say so, so that addressing and branches stay scalar
+  s = __builtin_amdgcn_readfirstlane(s);
+  j = __builtin_amdgcn_readfirstlane(j);
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
   const int col = lane & 15;                     // head column / K row within a half
   const int grp = lane >> 4;                     // 16-lane group
   const int G = a.group;
@@ -176,65 +210,72 @@ __global__ __launch_bounds__(NW * 64) void partition_kernel(Params a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + w * kTile * VS;
-  const int32_t* trow = PAGED ? a.block_table + (int64_t)s * a.max_blocks : nullptr;
-  const int64_t tok_stride = (int64_t)a.h_kv * D;   // elements between consecutive tokens
+  const int64_t trow = (int64_t)s * a.max_blocks;
+  const uint32_t tok_stride = (uint32_t)a.h_kv * D;   // elements between consecutive tokens
   const int bs_mask = (1 << a.bs_shift) - 1;
 
-  for (int tb = t0 + w * kTile; tb < t1; tb += NW * kTile) {
-    // element offset of the first row of each 16-token half (tiles are 16-aligned,
-    // block_size >= 16, so a half never straddles two physical blocks)
-    int64_t base[2];
+  struct Tile {
+    uint4_t k[2][KK];
+    uint4_t v[NIT];
+  };
+
+  // Issue every global load of the tile starting at token tb (tb < t1).  Each
+  // 16-token half has a wave-uniform base pointer; lanes add small 32-bit
+  // offsets.  Rows past t1 are clamped to the last live token of the segment,
+  // so every load is in bounds and unconditional; those rows are masked
+  // afterwards (score -inf, hence a zero weight on a finite V row).
+  auto load = [&](Tile& T, int tb) {
+    const uint16_t* kb[2];
+    const uint16_t* vb[2];
+    int last[2];                                  // last live row of each half
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int th = tb + 16 * hb;
+      const int th = min(tb + 16 * hb, t1 - 1);   // 16-aligned unless past t1
+      last[hb] = min(15, t1 - 1 - th);
+      int64_t base;
       if constexpr (PAGED) {
-        const int32_t blk = th < t1 ? trow[th >> a.bs_shift] : 0;
-        base[hb] = ((((int64_t)blk << a.bs_shift) + (th & bs_mask)) * a.h_kv + j) * D;
+        const int32_t blk = load_const(a.block_table, trow + (th >> a.bs_shift));
+        base = ((((int64_t)blk << a.bs_shift) + (th & bs_mask)) * a.h_kv + j) * D;
       } else {
-        base[hb] = (((int64_t)s * a.s_kv + th) * a.h_kv + j) * D;
+        base = (((int64_t)s * a.s_kv + th) * a.h_kv + j) * D;
       }
+      kb[hb] = a.k + base;
+      vb[hb] = a.v + base;
     }
-
-    // ---- issue all global loads of the tile first
-    uint4_t vreg[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int r = it * RPI + lane / CH;
-      const int c = lane % CH;
-      vreg[it] = (tb + r < t1)
-          ? *reinterpret_cast<const uint4_t*>(a.v + base[r >> 4] + (r & 15) * tok_stride + c * 8)
-          : uint4_t{0u, 0u, 0u, 0u};
+      const int hb = r >> 4;                      // uniform per instruction
+      const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
+      T.v[it] = *reinterpret_cast<const uint4_t*>(vb[hb] + off);
     }
-    uint4_t kop[2][KK];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const bool ok = tb + 16 * hb + col < t1;
-      const uint16_t* krow = a.k + base[hb] + col * tok_stride;
+      const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kop[hb][kk] = ok ? *reinterpret_cast<const uint4_t*>(krow + 8 * (kk * 4 + grp))
-                         : uint4_t{0u, 0u, 0u, 0u};
+        T.k[hb][kk] = *reinterpret_cast<const uint4_t*>(kb[hb] + roff + 8 * (kk * 4 + grp));
     }
+  };
 
-    // ---- stage V (row-major, padded rows)
+  // fold the tile starting at token tb into (m_run, l_run, acc)
+  auto compute = [&](const Tile& T, int tb) {
+    // stage V: row r, chunk c at position c ^ swizzle(r)
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int r = it * RPI + lane / CH;
-      const int c = lane % CH;
-      *reinterpret_cast<uint4_t*>(vt + r * VS + c * 8) = vreg[it];
+      const int pos = (lane % CH) ^ v_swizzle(r);
+      *reinterpret_cast<uint4_t*>(vt + r * D + pos * 8) = T.v[it];
     }
-
-    // ---- scores S^T = K . Q^T
+    // scores S^T = K . Q^T
     float4_t sc[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       sc[hb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc[hb] = DT::mfma(kop[hb][kk], qop[kk], sc[hb]);
+      for (int kk = 0; kk < KK; ++kk) sc[hb] = DT::mfma(T.k[hb][kk], qop[kk], sc[hb]);
     }
-
-    // ---- online softmax (base 2); lane holds tokens slot_token(grp, e) of head col
+    // online softmax (base 2); the lane holds tokens slot_token(grp, e) of head col
     float x[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -248,7 +289,6 @@ __global__ __launch_bounds__(NW * 64) void partition_kernel(Params a) {
     const float m_new = fmaxf(m_run, mx);          // finite: the tile holds a live token
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-
     // P as a hi + lo pair in the storage dtype (about twice its significand)
     uint32_t phi[4], plo[4];
     float psum = 0.f;
@@ -270,16 +310,17 @@ __global__ __launch_bounds__(NW * 64) void partition_kernel(Params a) {
     l_run = l_run * alpha + psum;
     const uint4_t phi4{phi[0], phi[1], phi[2], phi[3]};
     const uint4_t plo4{plo[0], plo[1], plo[2], plo[3]};
-
-    // ---- O^T += V^T . P^T, V^T read transposed from the staged tile
+    // O^T += V^T . P^T, V^T read transposed from the staged tile
     wave_lds_fence();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t vv[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t lo = vt[slot_token(grp, 2 * e2) * VS + 16 * nb + col];
-        const uint32_t hi = vt[slot_token(grp, 2 * e2 + 1) * VS + 16 * nb + col];
+        const int d = 16 * nb + col;
+        const int ra = slot_token(grp, 2 * e2), rb = slot_token(grp, 2 * e2 + 1);
+        const uint32_t lo = vt[ra * D + (((d >> 3) ^ v_swizzle(ra)) << 3) + (d & 7)];
+        const uint32_t hi = vt[rb * D + (((d >> 3) ^ v_swizzle(rb)) << 3) + (d & 7)];
         vv[e2] = lo | (hi << 16);
       }
       const uint4_t vop{vv[0], vv[1], vv[2], vv[3]};
@@ -287,109 +328,318 @@ __global__ __launch_bounds__(NW * 64) void partition_kernel(Params a) {
       acc[nb] = DT::mfma(vop, phi4, acc[nb]);
       acc[nb] = DT::mfma(vop, plo4, acc[nb]);
     }
-    wave_lds_fence();
+    wave_lds_fence();                               // reads retire before the next stores
+  };
+
+  // ---- token loop: two register tiles ping-ponged so that the next tile's
+  //      loads are in flight while the current one is computed.  The steady
+  //      state issues its loads unconditionally and the last one or two tiles
+  //      are peeled, so every wait count the compiler derives is static; the
+  //      scheduling barriers keep each prefetch ahead of the compute it
+  //      overlaps.
+  int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
+  if (n > 0) {
+    Tile A, B;
+    int tb = t0;
+    load(A, tb);
+    while (n >= 3) {
+      load(B, tb + kTile);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, tb);
+      load(A, tb + 2 * kTile);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B, tb + kTile);
+      tb += 2 * kTile;
+      n -= 2;
+    }
+    if (n == 2) {
+      load(B, tb + kTile);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, tb);
+      compute(B, tb + kTile);
+    } else {
+      compute(A, tb);
+    }
   }
 
-  // ---- merge the NW waves in LDS: red[(w*D + d)*kRedStride + head], with
-  //      columns 16..19 of rows 0..3 holding m and of rows 4..7 holding l
+  // ---- epilogue: each lane owns head col, d = 16 nb + 4 grp + r
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);
+  if (col >= G) return;
+  if (complete) {
+    uint16_t* dst = a.out + ((int64_t)s * a.h_q + head0 + col) * D + 4 * grp;
+    const bool empty = t1 <= t0;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      red[(w * D + 16 * nb + 4 * grp + r) * kRedStride + col] = acc[nb][r];
-  if (grp == 0) {
-    red[(w * D + (col >> 2)) * kRedStride + 16 + (col & 3)] = m_run;
-    red[(w * D + 4 + (col >> 2)) * kRedStride + 16 + (col & 3)] = l_run;
-  }
-  __syncthreads();
-
-  for (int idx = threadIdx.x; idx < G * CH; idx += NW * 64) {
-    const int g = idx / CH;
-    const int d0 = (idx % CH) * 8;
-    float mw[NW];
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-      mw[u] = red[(u * D + (g >> 2)) * kRedStride + 16 + (g & 3)];
-      M = fmaxf(M, mw[u]);
-    }
-    float lsum = 0.f;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-      if (mw[u] == -INFINITY) continue;          // a wave that saw no token
-      const float aw = __builtin_amdgcn_exp2f(mw[u] - M);
-      lsum += aw * red[(u * D + 4 + (g >> 2)) * kRedStride + 16 + (g & 3)];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] += aw * red[(u * D + d0 + e) * kRedStride + g];
-    }
-    const int64_t row = (int64_t)s * a.h_q + head0 + g;
-    if (!split) {
-      uint32_t packed[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t lo = L > 0 ? DT::narrow(o[2 * e2] / lsum) : 0u;
-        const uint32_t hi = L > 0 ? DT::narrow(o[2 * e2 + 1] / lsum) : 0u;
-        packed[e2] = lo | (hi << 16);
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t w01, w23;
+      if (empty) {
+        w01 = w23 = 0u;
+      } else {
+        w01 = DT::narrow(acc[nb][0] / l_run) | (DT::narrow(acc[nb][1] / l_run) << 16);
+        w23 = DT::narrow(acc[nb][2] / l_run) | (DT::narrow(acc[nb][3] / l_run) << 16);
       }
-      *reinterpret_cast<uint4_t*>(a.out + row * D + d0) =
-          uint4_t{packed[0], packed[1], packed[2], packed[3]};
+      *reinterpret_cast<uint2*>(dst + 16 * nb) = make_uint2(w01, w23);
+    }
+  } else {
+    float* dst = po + (int64_t)col * o_stride + 4 * grp;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<float4_t*>(dst + 16 * nb) = acc[nb];
+    if (grp == 0) pml[(int64_t)col * ml_stride] = make_float2(m_run, l_run);
+  }
+}
+
+// ------------------------------------------------- fixed-partition kernel --
+//
+// One workgroup per (partition p, head group, sequence s), one wave per KV
+// head of the group; the kernel-map page's decomposition: a sequence of at
+// most v1_max_ctx tokens is one partition written directly, a longer one is
+// cut into ceil(L / part_size) partitions whose partials land at [s, i, p].
+
+template <class DT, int D, bool PAGED>
+__global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_fixed_kernel(Params a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = blockIdx.x % a.max_parts;
+  const int rest = blockIdx.x / a.max_parts;
+  const int hg = rest % a.n_groups;
+  const int s = rest / a.n_groups;
+  const int L = seq_len<PAGED>(a, s);
+  const bool split = L > a.v1_max_ctx;
+  const int n_part = split ? (L + a.part_size - 1) / a.part_size : 1;
+  if (p >= n_part) return;                       // uniform over the workgroup
+  const int t0 = split ? p * a.part_size : 0;
+  const int t1 = split ? min(t0 + a.part_size, L) : L;
+  const int j = hg * a.hpw + w;
+  const int64_t row0 = (int64_t)s * a.h_q + j * a.group;
+  wave_segment<DT, D, PAGED>(a, smem + w * Geo<D>::V_TILE, s, j, t0, t1, !split,
+                             a.part_ml + row0 * a.max_parts + p, a.max_parts,
+                             a.part_o + (row0 * a.max_parts + p) * D, (int64_t)a.max_parts * D);
+}
+
+// ------------------------------------------------------- balanced kernel --
+//
+// Persistent grid of W workgroups.  The (sequence, head group) ranges are
+// laid end to end in 32-token tiles (range (s, g) holds ceil(L_s / 32)
+// tiles, at least one); workgroup w owns the tiles [w C, (w+1) C) with
+// C = max(ceil(total / W), kMinChunkTiles).  A range is processed by the
+// workgroups whose shares it overlaps, one segment each; a range of at most
+// v1_max_ctx tokens is never split and belongs to the workgroup its first tile
+// falls in.  A range that ends up in one segment is written directly; the
+// segments of a split range write fp32 partials to per-workgroup slots
+// (2w for the range the share starts in, 2w + 1 for the one it ends in) and
+// the range's first segment records (first workgroup, last workgroup, first
+// slot) for the merge kernel.
+
+// The prefix lives in LDS, which the compiler treats as per-lane data; every
+// lane reads the same entry, so readfirstlane keeps the scheduling arithmetic
+// (and everything derived from it) in scalar registers.
+template <bool PAGED>
+__device__ __forceinline__ int64_t range_prefix(const Params& a, const int32_t* pref, int s) {
+  if constexpr (PAGED)
+    return __builtin_amdgcn_readfirstlane(pref[s]);
+  else
+    return (int64_t)s * a.n_groups * seq_tiles(a.s_kv);
+}
+
+template <class DT, int D, bool PAGED>
+__global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_kernel(Params a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles, then the prefix
+  __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;                // = hpw
+  uint16_t* const vt = smem + w * Geo<D>::V_TILE;
+  int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * Geo<D>::V_TILE);
+
+  // ---- paged: pref[s] = n_groups * (tiles of sequences < s); arithmetic when contiguous
+  int64_t total;
+  if constexpr (PAGED) {
+    int32_t run = 0;
+    for (int base = 0; base < a.num_seqs; base += blockDim.x) {
+      const int s = base + threadIdx.x;
+      int32_t v = 0;
+      if (s < a.num_seqs) {
+        const int L = min(max(a.ctx_lens[s], 0), a.max_ctx);
+        v = a.n_groups * seq_tiles(L);
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+      }
+      if (lane == 63) wave_tot[w] = v;
+      __syncthreads();
+      int32_t before = run;
+      for (int u = 0; u < w; ++u) before += wave_tot[u];
+      if (s < a.num_seqs) pref[s + 1] = before + v;
+      for (int u = 0; u < nw; ++u) run += wave_tot[u];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) pref[0] = 0;
+    __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(run);
+  } else {
+    total = (int64_t)a.num_seqs * a.n_groups * seq_tiles(a.s_kv);
+  }
+
+  const int64_t chunk = max((total + gridDim.x - 1) / gridDim.x, (int64_t)kMinChunkTiles);
+  const int64_t x0 = (int64_t)blockIdx.x * chunk;
+  if (x0 >= total) return;                       // uniform: no share
+  const int64_t x1 = min(x0 + chunk, total);
+
+  // ---- first sequence whose ranges reach past x0 (largest s with prefix <= x0)
+  int s = 0;
+  {
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (range_prefix<PAGED>(a, pref, mid) <= x0) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+  }
+  int L = seq_len<PAGED>(a, s);
+  int nt = seq_tiles(L);
+  int hg = (int)((x0 - range_prefix<PAGED>(a, pref, s)) / nt);
+  const int wg = blockIdx.x;
+  const int heads = a.hpw * a.group;             // query heads per head group
+
+  for (;;) {
+    const int64_t rs = range_prefix<PAGED>(a, pref, s) + (int64_t)hg * nt;
+    if (rs >= x1) break;
+    const int64_t re = rs + nt;
+    const int r = s * a.n_groups + hg;
+    const int j = hg * a.hpw + w;
+    if (L <= a.v1_max_ctx) {
+      if (rs >= x0) {                            // owned: the whole range, never split
+        wave_segment<DT, D, PAGED>(a, vt, s, j, 0, L, true, nullptr, 0, nullptr, 0);
+        if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
+      }
     } else {
-      float* dst = a.part_o + (row * a.max_parts + p) * D + d0;
-      *reinterpret_cast<float4_t*>(dst) = float4_t{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<float4_t*>(dst + 4) = float4_t{o[4], o[5], o[6], o[7]};
-      if (d0 == 0) a.part_ml[row * a.max_parts + p] = make_float2(M, lsum);
+      const int64_t sa = max(rs, x0) - rs;
+      const int64_t sb = min(re, x1) - rs;
+      const int t0 = (int)(sa * kTile);
+      const int t1 = (int)min(sb * kTile, (int64_t)L);
+      if (sa == 0 && sb == nt) {
+        wave_segment<DT, D, PAGED>(a, vt, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
+        if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
+      } else {
+        const int slot = 2 * wg + (rs <= x0 ? 0 : 1);
+        const int64_t hrow = (int64_t)slot * heads + w * a.group;
+        wave_segment<DT, D, PAGED>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
+                                   a.part_o + hrow * D, D);
+        if (sa == 0 && threadIdx.x == 0)
+          a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
+      }
+    }
+    if (++hg == a.n_groups) {
+      hg = 0;
+      if (++s == a.num_seqs) break;
+      L = seq_len<PAGED>(a, s);
+      nt = seq_tiles(L);
     }
   }
 }
 
-// ---------------------------------------------------------- merge kernel --
+// ----------------------------------------------------------- merge kernel --
+//
+// Persistent grid striding over (sequence, query head).  A head whose sequence
+// was split is merged by the whole workgroup: the n-ary form of the
+// decode-long page's "_merge_running" over its n partials, then its "Final
+// normalise + store".  The 256 threads take 16 interleaved subsets of the
+// partials times 16 slices of d, and the 16 subsets are summed in a fixed
+// order, so the result does not depend on scheduling.
 
-template <class DT, int D, bool PAGED>
-__global__ __launch_bounds__(256) void merge_kernel(Params a) {
-  constexpr int E = D / 64;                       // output elements per lane
-  const int lane = threadIdx.x & 63;
-  const int heads4 = (a.h_q + 3) >> 2;
-  const int s = blockIdx.x / heads4;
-  const int i = (blockIdx.x % heads4) * 4 + (threadIdx.x >> 6);
-  if (i >= a.h_q) return;                         // no barriers below: per-wave exit is safe
-  const int L = seq_len<PAGED>(a, s);
-  if (L <= a.v1_max_ctx) return;                  // written by the partition kernel
-  const int n = (L + a.part_size - 1) / a.part_size;
-  const int64_t row = (int64_t)s * a.h_q + i;
-  const float2* ml = a.part_ml + row * a.max_parts;
-  const float* po = a.part_o + row * a.max_parts * D + lane * E;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = 16;                  // partial subsets per head
 
-  float M = -INFINITY;
-  for (int pp = lane; pp < n; pp += 64) M = fmaxf(M, ml[pp].x);
+template <class DT, int D, bool PAGED, bool BALANCED>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
+  constexpr int E = D / 16;                       // d elements per thread
+  __shared__ __attribute__((aligned(16))) float red_o[kMergeGroups][D];
+  __shared__ float red_l[kMergeGroups];
+  __shared__ float red_m[kMergeThreads / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int kg = t / 16;                          // partial subset
+  const int ds = t % 16;                          // d slice
+  const int heads = a.hpw * a.group;
+  const int items = a.num_seqs * a.h_q;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int s = item / a.h_q;
+    const int i = item % a.h_q;
+    // ---- the partial rows of (s, i), or skip a head written in one pass
+    int n;
+    int64_t base = 0;
+    int4 d{0, 0, 0, 0};
+    if constexpr (BALANCED) {
+      d = a.desc[s * a.n_groups + i / heads];
+      d.x = __builtin_amdgcn_readfirstlane(d.x);
+      d.y = __builtin_amdgcn_readfirstlane(d.y);
+      d.z = __builtin_amdgcn_readfirstlane(d.z);
+      if (d.y == d.x) continue;                   // uniform
+      n = d.y - d.x + 1;
+    } else {
+      const int L = seq_len<PAGED>(a, s);
+      if (L <= a.v1_max_ctx) continue;            // uniform
+      n = (L + a.part_size - 1) / a.part_size;
+      base = ((int64_t)s * a.h_q + i) * a.max_parts;
+    }
+    const int local = i % heads;
+    auto row = [&](int k) -> int64_t {
+      if constexpr (BALANCED)
+        return (int64_t)(k == 0 ? d.z : 2 * (d.x + k)) * heads + local;
+      else
+        return base + k;
+    };
+    // ---- M = max_k m_k
+    float M = -INFINITY;
+    for (int k = t; k < n; k += kMergeThreads) M = fmaxf(M, a.part_ml[row(k)].x);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-
-  // fixed partition order: the result does not depend on scheduling
-  float lsum = 0.f;
-  float o[E];
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0) red_m[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    // ---- this thread's subset: partials kg, kg + 16, ...; d in [ds*E, ds*E + E)
+    float o[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int pp = 0; pp < n; ++pp) {
-    const float2 t = ml[pp];
-    const float wgt = __builtin_amdgcn_exp2f(t.x - M);
-    lsum += wgt * t.y;
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+    float lsum = 0.f;
+    for (int k = kg; k < n; k += kMergeGroups) {
+      const int64_t rw = row(k);
+      const float2 t2 = a.part_ml[rw];
+      const float wgt = __builtin_amdgcn_exp2f(t2.x - M);
+      lsum += wgt * t2.y;
+      const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + ds * E);
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += wgt * po[(int64_t)pp * D + e];
+      for (int e4 = 0; e4 < E / 4; ++e4) {
+        const float4_t v = src[e4];
+        o[4 * e4 + 0] += wgt * v[0];
+        o[4 * e4 + 1] += wgt * v[1];
+        o[4 * e4 + 2] += wgt * v[2];
+        o[4 * e4 + 3] += wgt * v[3];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) red_o[kg][ds * E + e] = o[e];
+    if (ds == 0) red_l[kg] = lsum;
+    __syncthreads();
+    if (t < D) {
+      float acc = 0.f, l = 0.f;
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) {
+        acc += red_o[g][t];
+        l += red_l[g];
+      }
+      a.out[((int64_t)s * a.h_q + i) * D + t] = static_cast<uint16_t>(DT::narrow(acc / l));
+    }
+    __syncthreads();                               // LDS is reused by the next item
   }
-  uint16_t* dst = a.out + row * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) dst[e] = static_cast<uint16_t>(DT::narrow(o[e] / lsum));
 }
 
 // ------------------------------------------------------------------ host --
 
-constexpr int32_t kDefaultPartition = 1024;
-constexpr int32_t kDefaultV1Max = 1024;
+constexpr int32_t kDefaultV1Max = 256;
+constexpr int32_t kFallbackPartition = 512;
 
 struct Problem {
   bool paged;
@@ -415,58 +665,141 @@ struct Problem {
 };
 
 bool aligned(const void* ptr, uintptr_t n) { return (reinterpret_cast<uintptr_t>(ptr) & (n - 1)) == 0; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 gqa_status_t resolve_policy(const gqa_policy_t* in, gqa_policy_t* out) {
   if (in == nullptr)
     gqa_policy_default(out);
   else
     *out = *in;
-  if (out->partition_size < kTile || out->partition_size > (1 << 20) ||
-      out->partition_size % kTile != 0 || out->v1_max_ctx < 0 || out->phases < 0 ||
-      out->phases > 3 || out->reserved != 0)
+  const bool balanced = out->partition_size == 0;
+  if ((!balanced && (out->partition_size < kTile || out->partition_size > (1 << 20) ||
+                     out->partition_size % kTile != 0)) ||
+      out->v1_max_ctx < 0 || out->phases < 0 || out->phases > 3 || out->reserved != 0)
     return GQA_ERR_BAD_POLICY;
   if (out->phases == 0) out->phases = 3;
   return GQA_OK;
 }
 
-int parts_for(int max_ctx, const gqa_policy_t& pol) {
-  if (max_ctx <= pol.v1_max_ctx) return 1;
-  return (int)(((int64_t)max_ctx + pol.partition_size - 1) / pol.partition_size);
+// KV heads per workgroup: the largest divisor of h_kv that is at most 8, so
+// that a workgroup's waves read whole groups of adjacent heads of a token.
+int heads_per_group(int h_kv) {
+  for (int h = std::min(h_kv, kMaxHeadsPerGroup); h > 1; --h)
+    if (h_kv % h == 0) return h;
+  return 1;
 }
 
-size_t workspace_for(int num_seqs, int h_q, int d, int max_ctx, const gqa_policy_t& pol) {
-  if (max_ctx <= pol.v1_max_ctx) return 0;
-  const size_t rows = (size_t)num_seqs * (size_t)h_q * (size_t)parts_for(max_ctx, pol);
-  const size_t ml = (rows * sizeof(float2) + 255) & ~(size_t)255;
-  return ml + rows * (size_t)d * sizeof(float);
+// How a call is decomposed once the sizes are known.
+struct Plan {
+  bool balanced;
+  int hpw;            // KV heads (waves) per workgroup
+  int n_groups;       // h_kv / hpw
+  int part_size;      // fixed mode
+  int max_parts;      // fixed mode
+  bool can_split;     // some sequence may exceed v1_max_ctx
+  size_t ws_desc, ws_ml, ws_o, ws_total;   // byte sizes of the workspace regions
+};
+
+int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
+  return (int64_t)num_seqs * n_groups * std::max<int64_t>(1, ((int64_t)max_ctx + kTile - 1) / kTile);
+}
+
+Plan make_plan(int num_seqs, int h_q, int h_kv, int d, int max_ctx, const gqa_policy_t& pol) {
+  Plan pl{};
+  pl.hpw = heads_per_group(h_kv);
+  pl.n_groups = h_kv / pl.hpw;
+  pl.can_split = max_ctx > pol.v1_max_ctx;
+  // the balanced scheduler keeps its per-sequence prefix in LDS as int32
+  pl.balanced = pol.partition_size == 0 && num_seqs <= kMaxSeqsBalanced &&
+                upper_tiles(num_seqs, pl.n_groups, max_ctx) < (int64_t)INT32_MAX / 2;
+  pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
+  pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
+  if (!pl.can_split) return pl;
+  if (pl.balanced) {
+    const size_t rows = (size_t)2 * kMaxGrid * pl.hpw * (h_q / h_kv);
+    pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
+    pl.ws_ml = align256(rows * sizeof(float2));
+    pl.ws_o = rows * (size_t)d * sizeof(float);
+  } else {
+    const size_t rows = (size_t)num_seqs * h_q * pl.max_parts;
+    pl.ws_desc = 0;
+    pl.ws_ml = align256(rows * sizeof(float2));
+    pl.ws_o = rows * (size_t)d * sizeof(float);
+  }
+  pl.ws_total = pl.ws_desc + pl.ws_ml + pl.ws_o;
+  return pl;
+}
+
+// Resident workgroups for a kernel, cached per (device, kernel, block, dynamic LDS).
+int resident_grid(const void* kernel, int block, size_t dyn_lds) {
+  struct Entry { int dev; const void* k; int block; size_t lds; int grid; };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int n_cache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int e = 0; e < n_cache; ++e)
+      if (cache[e].dev == dev && cache[e].k == kernel && cache[e].block == block &&
+          cache[e].lds == dyn_lds)
+        return cache[e].grid;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, dyn_lds) != hipSuccess)
+    return 0;
+  const int grid = std::max(1, cus * std::max(1, per_cu));
+  std::lock_guard<std::mutex> lock(mu);
+  if (n_cache < 64) cache[n_cache++] = Entry{dev, kernel, block, dyn_lds, grid};
+  return grid;
 }
 
 template <class DT, int D, bool PAGED>
-gqa_status_t launch_typed(const Params& prm, int grid_parts, int grid_merge, int phases,
-                          hipStream_t stream) {
+gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStream_t stream) {
   Params local = prm;
   void* args[] = {&local};
-  if ((phases & 1) && grid_parts > 0) {
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_kernel<DT, D, PAGED, kWaves>),
-                        dim3(grid_parts), dim3(kWaves * 64), args, 0, stream) != hipSuccess)
-      return GQA_ERR_LAUNCH;
+  const int block = 64 * pl.hpw;
+  const size_t tiles_lds = (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t);
+  if (phases & 1) {
+    if (pl.balanced) {
+      const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED>);
+      const size_t dyn = tiles_lds + (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
+      const int resident = resident_grid(kern, block, dyn);
+      if (resident <= 0) return GQA_ERR_LAUNCH;
+      const int64_t want =
+          (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
+      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxGrid, resident, want}));
+      if (hipLaunchKernel(kern, dim3(grid), dim3(block), args, dyn, stream) != hipSuccess)
+        return GQA_ERR_LAUNCH;
+    } else {
+      const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;
+      if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED>),
+                          dim3((unsigned)grid), dim3(block), args, tiles_lds, stream) != hipSuccess)
+        return GQA_ERR_LAUNCH;
+    }
   }
-  if ((phases & 2) && grid_merge > 0) {
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED>),
-                        dim3(grid_merge), dim3(256), args, 0, stream) != hipSuccess)
+  if ((phases & 2) && pl.can_split) {
+    const void* kern = pl.balanced ? reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, true>)
+                                   : reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, false>);
+    const int resident = resident_grid(kern, kMergeThreads, 0);
+    if (resident <= 0) return GQA_ERR_LAUNCH;
+    const int64_t items = (int64_t)prm.num_seqs * prm.h_q;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, resident));
+    if (hipLaunchKernel(kern, dim3(grid), dim3(kMergeThreads), args, 0, stream) != hipSuccess)
       return GQA_ERR_LAUNCH;
   }
   return GQA_OK;
 }
 
 template <class DT>
-gqa_status_t launch_dtype(const Problem& pb, const Params& prm, int gp, int gm, int ph,
+gqa_status_t launch_dtype(const Problem& pb, const Params& prm, const Plan& pl, int ph,
                           hipStream_t st) {
   if (pb.d == 64)
-    return pb.paged ? launch_typed<DT, 64, true>(prm, gp, gm, ph, st)
-                    : launch_typed<DT, 64, false>(prm, gp, gm, ph, st);
-  return pb.paged ? launch_typed<DT, 128, true>(prm, gp, gm, ph, st)
-                  : launch_typed<DT, 128, false>(prm, gp, gm, ph, st);
+    return pb.paged ? launch_typed<DT, 64, true>(prm, pl, ph, st)
+                    : launch_typed<DT, 64, false>(prm, pl, ph, st);
+  return pb.paged ? launch_typed<DT, 128, true>(prm, pl, ph, st)
+                  : launch_typed<DT, 128, false>(prm, pl, ph, st);
 }
 
 gqa_status_t run(const Problem& pb) {
@@ -491,10 +824,10 @@ gqa_status_t run(const Problem& pb) {
   const int64_t max_ctx64 = pb.paged ? (int64_t)pb.max_blocks * pb.block_size : pb.s_kv;
   if (max_ctx64 > (1 << 30)) return GQA_ERR_BAD_SHAPE;
   const int max_ctx = (int)max_ctx64;
-  const int max_parts = parts_for(max_ctx, pol);
-  const int64_t grid_parts = (int64_t)max_parts * pb.h_kv * pb.num_seqs;
-  const int64_t grid_merge = (max_ctx > pol.v1_max_ctx) ? (int64_t)((pb.h_q + 3) / 4) * pb.num_seqs : 0;
-  if (grid_parts > INT32_MAX || grid_merge > INT32_MAX) return GQA_ERR_BAD_SHAPE;
+  const Plan pl = make_plan(pb.num_seqs, pb.h_q, pb.h_kv, pb.d, max_ctx, pol);
+  if (!pl.balanced && (int64_t)pl.max_parts * pl.n_groups * pb.num_seqs > INT32_MAX)
+    return GQA_ERR_BAD_SHAPE;
+  if ((int64_t)pb.h_q * pb.num_seqs > INT32_MAX) return GQA_ERR_BAD_SHAPE;
   if (pb.num_seqs == 0) return GQA_OK;
 
   // ---- pointers
@@ -506,9 +839,8 @@ gqa_status_t run(const Problem& pb) {
     return GQA_ERR_MISALIGNED;
   if (pb.paged && (!aligned(pb.block_table, 4) || !aligned(pb.ctx_lens, 4)))
     return GQA_ERR_MISALIGNED;
-  const size_t need = workspace_for(pb.num_seqs, pb.h_q, pb.d, max_ctx, pol);
-  if (need > 0) {
-    if (!pb.ws || pb.ws_bytes < need) return GQA_ERR_WORKSPACE;
+  if (pl.ws_total > 0) {
+    if (!pb.ws || pb.ws_bytes < pl.ws_total) return GQA_ERR_WORKSPACE;
     if (!aligned(pb.ws, 256)) return GQA_ERR_MISALIGNED;
   }
 
@@ -520,27 +852,30 @@ gqa_status_t run(const Problem& pb) {
   prm.out = static_cast<uint16_t*>(pb.out);
   prm.block_table = pb.block_table;
   prm.ctx_lens = pb.ctx_lens;
-  const size_t rows = (size_t)pb.num_seqs * pb.h_q * max_parts;
-  prm.part_ml = need ? static_cast<float2*>(pb.ws) : nullptr;
-  prm.part_o = need ? reinterpret_cast<float*>(static_cast<char*>(pb.ws) +
-                                               ((rows * sizeof(float2) + 255) & ~(size_t)255))
-                    : nullptr;
+  if (pl.ws_total > 0) {
+    char* ws = static_cast<char*>(pb.ws);
+    prm.desc = pl.ws_desc ? reinterpret_cast<int4*>(ws) : nullptr;
+    prm.part_ml = reinterpret_cast<float2*>(ws + pl.ws_desc);
+    prm.part_o = reinterpret_cast<float*>(ws + pl.ws_desc + pl.ws_ml);
+  }
   prm.num_seqs = pb.num_seqs;
   prm.h_q = pb.h_q;
   prm.h_kv = pb.h_kv;
   prm.group = G;
+  prm.hpw = pl.hpw;
+  prm.n_groups = pl.n_groups;
   prm.s_kv = pb.s_kv;
   prm.max_blocks = pb.max_blocks;
   prm.bs_shift = bs_shift;
   prm.max_ctx = max_ctx;
-  prm.part_size = pol.partition_size;
-  prm.v1_max_ctx = pol.v1_max_ctx;
-  prm.max_parts = max_parts;
+  prm.part_size = pl.part_size;
+  // with no workspace nothing may split: the single-pass bound covers every sequence
+  prm.v1_max_ctx = pl.can_split ? pol.v1_max_ctx : max_ctx;
+  prm.max_parts = pl.max_parts;
   prm.c = pb.scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(pb.stream);
-  if (pb.dtype == GQA_F16)
-    return launch_dtype<F16>(pb, prm, (int)grid_parts, (int)grid_merge, pol.phases, st);
-  return launch_dtype<BF16>(pb, prm, (int)grid_parts, (int)grid_merge, pol.phases, st);
+  if (pb.dtype == GQA_F16) return launch_dtype<F16>(pb, prm, pl, pol.phases, st);
+  return launch_dtype<BF16>(pb, prm, pl, pol.phases, st);
 }
 
 }  // namespace
@@ -549,7 +884,7 @@ extern "C" {
 
 void gqa_policy_default(gqa_policy_t* p) {
   if (!p) return;
-  p->partition_size = kDefaultPartition;
+  p->partition_size = 0;
   p->v1_max_ctx = kDefaultV1Max;
   p->phases = 0;
   p->reserved = 0;
@@ -563,12 +898,13 @@ void gqa_policy_pages(gqa_policy_t* p) {
   p->reserved = 0;
 }
 
-size_t gqa_decode_workspace_size(int num_seqs, int h_q, int d_head, int max_ctx,
+size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, int max_ctx,
                                  const gqa_policy_t* policy) {
   gqa_policy_t pol;
   if (resolve_policy(policy, &pol) != GQA_OK) return 0;
-  if (num_seqs < 0 || h_q <= 0 || d_head <= 0 || max_ctx < 0) return 0;
-  return workspace_for(num_seqs, h_q, d_head, max_ctx, pol);
+  if (num_seqs < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || d_head <= 0 || max_ctx < 0)
+    return 0;
+  return make_plan(num_seqs, h_q, h_kv, d_head, max_ctx, pol).ws_total;
 }
 
 gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -37,9 +37,10 @@
  * partials and the merge are fp32; the output is rounded to nearest-even.
  *
  * Ownership.  The caller owns every buffer, the workspace included.  The
- * library never allocates, frees or synchronises and keeps no device state;
- * calls on different streams with distinct workspaces and outputs may run
- * concurrently.
+ * library never allocates, frees or synchronises and keeps no device state
+ * (it caches, per device and kernel, how many workgroups fit on the device
+ * at once); calls on different streams with distinct workspaces and outputs
+ * may run concurrently.
  *
  * Errors.  Every argument is checked on the host before any HIP call; a
  * failed check returns its status with nothing launched.  A failed launch
@@ -79,17 +80,28 @@ typedef enum gqa_status {
 } gqa_status_t;
 
 /*
- * Launch policy.  partition_size is the number of tokens one workgroup
- * covers for a split sequence (a multiple of 32 in [32, 1 << 20]);
- * v1_max_ctx (>= 0) is the longest sequence handled as one partition with no
- * merge.  The decomposition follows the kernel-map page ("paged_attention_v1"
- * for short contexts, "paged_attention_v2" above the threshold) with sizes
- * chosen for MI355X by gqa_policy_default(); gqa_policy_pages() gives the
+ * Launch policy.
+ *
+ * partition_size == 0 selects the balanced decomposition (the MI355X
+ * default): a persistent grid of as many workgroups as the device holds at
+ * once, each owning an equal, 32-token-aligned share of all (sequence, KV
+ * head) token ranges laid end to end.  A range that falls inside one share is
+ * computed and written in one pass; a range that spans several shares is
+ * split at the share boundaries and its partials are merged.  A sequence of
+ * at most v1_max_ctx tokens is never split.
+ *
+ * partition_size > 0 (a multiple of 32, at most 1 << 20) selects the
+ * kernel-map page's fixed decomposition ("paged_attention_v1" up to
+ * v1_max_ctx tokens, "paged_attention_v2" with partitions of partition_size
+ * tokens above it), one workgroup per partition; gqa_policy_pages() gives the
  * policy page's AttentionConfig values (partition 512, threshold 8192).
- * phases selects which kernels a call launches: 0 or 3 = both, 1 = partition
- * kernel only, 2 = merge kernel only (the merge then reads the partials a
- * phase-1 call with the same arguments left in the workspace); it exists so
- * that a caller can time the two kernels apart.
+ *
+ * v1_max_ctx >= 0.  phases selects which kernels a call launches: 0 or 3 =
+ * both, 1 = partition kernel only, 2 = merge kernel only (the merge then reads
+ * the partials a phase-1 call with the same arguments left in the
+ * workspace); it exists so that a caller can time the two kernels apart.
+ * The balanced decomposition needs num_seqs <= 8192; a larger batch uses the
+ * fixed one with 512-token partitions.
  */
 typedef struct gqa_policy {
   int32_t partition_size;
@@ -106,11 +118,12 @@ void gqa_policy_pages(gqa_policy_t* p);
 /*
  * Bytes of workspace gqa_decode / gqa_decode_contiguous need for these sizes
  * (max_ctx = max_blocks_per_seq * block_size, or s_kv).  0 when no sequence
- * can be split.  The workspace holds, per (sequence, query head, partition),
- * the fp32 pair (m, l) and the fp32 un-normalised O row.  policy NULL means
- * gqa_policy_default().  Returns 0 for invalid arguments.
+ * can be split.  The workspace holds fp32 partial triples (m, l, O) and, for
+ * the balanced decomposition, one 16-byte record per (sequence, KV head); its
+ * contents need no initialisation.  policy NULL means gqa_policy_default().
+ * Returns 0 for invalid arguments.
  */
-size_t gqa_decode_workspace_size(int num_seqs, int h_q, int d_head, int max_ctx,
+size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, int max_ctx,
                                  const gqa_policy_t* policy);
 
 /*

@@ -49,18 +49,29 @@ def test_policies(gq):
     d = gq.policy_default()
     p = gq.policy_pages()
     assert (p.partition_size, p.v1_max_ctx) == (512, 8192)
-    assert d.partition_size % 32 == 0 and d.v1_max_ctx >= 0
+    assert d.partition_size == 0 and d.v1_max_ctx >= 0       # balanced decomposition
 
 
 def test_workspace_size(gq):
     P = gq.policy_pages()
-    assert gq.workspace_size(4, 32, 128, 8192, P) == 0          # nothing can split
-    n = gq.workspace_size(4, 32, 128, 8193, P)                  # 17 partitions
+    assert gq.workspace_size(4, 32, 8, 128, 8192, P) == 0       # nothing can split
+    n = gq.workspace_size(4, 32, 8, 128, 8193, P)               # 17 partitions
     rows = 4 * 32 * 17
     assert n == ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
+    # balanced: a record per (sequence, head group of up to 8 KV heads) + two partial
+    # slots per workgroup (2048 workgroups at most), each holding the group's query heads
+    B = gq.policy_default()
+    assert gq.workspace_size(4, 32, 8, 128, B.v1_max_ctx, B) == 0
+    n = gq.workspace_size(4, 32, 8, 128, 4096, B)            # 8 KV heads: one group of 8
+    rows = 2 * 2048 * 32
+    assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
+    n = gq.workspace_size(3, 48, 12, 64, 4096, B)             # 12 KV heads: two groups of 6
+    rows = 2 * 2048 * 6 * 4
+    assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 64 * 4
     bad = gq.Policy(100, 0, 0, 0)
-    assert gq.workspace_size(4, 32, 128, 9000, bad) == 0
-    assert gq.workspace_size(-1, 32, 128, 9000, P) == 0
+    assert gq.workspace_size(4, 32, 8, 128, 9000, bad) == 0
+    assert gq.workspace_size(-1, 32, 8, 128, 9000, P) == 0
+    assert gq.workspace_size(4, 32, 5, 128, 9000, P) == 0        # h_q not a multiple of h_kv
 
 
 # Fake device pointers: never dereferenced, since every call below fails
@@ -112,15 +123,16 @@ def test_validation_errors(gq, kw, code):
 
 
 def test_policy_and_workspace_errors(gq):
-    for pol in (gq.Policy(100, 0, 0, 0), gq.Policy(0, 0, 0, 0), gq.Policy(512, -1, 0, 0),
-                gq.Policy(512, 0, 4, 0), gq.Policy(512, 0, 0, 1), gq.Policy(1 << 21, 0, 0, 0)):
+    for pol in (gq.Policy(100, 0, 0, 0), gq.Policy(16, 0, 0, 0), gq.Policy(-32, 0, 0, 0),
+                gq.Policy(512, -1, 0, 0), gq.Policy(0, -1, 0, 0), gq.Policy(512, 0, 4, 0),
+                gq.Policy(0, 0, -1, 0), gq.Policy(512, 0, 0, 1), gq.Policy(1 << 21, 0, 0, 0)):
         assert _call(gq, policy=pol) == ERR["POLICY"], pol
-    pol = gq.policy_pages(v1_max_ctx=0)          # everything splits: workspace needed
-    need = gq.workspace_size(2, 8, 128, 64, pol)
-    assert need > 0
-    assert _call(gq, policy=pol, ws=None) == ERR["WS"]
-    assert _call(gq, policy=pol, ws_bytes=need - 1) == ERR["WS"]
-    assert _call(gq, policy=pol, ws=A + 16) == ERR["ALIGN"]
+    for pol in (gq.policy_pages(v1_max_ctx=0), gq.policy_default(v1_max_ctx=0)):
+        need = gq.workspace_size(2, 8, 2, 128, 64, pol)           # everything may split
+        assert need > 0
+        assert _call(gq, policy=pol, ws=None) == ERR["WS"]
+        assert _call(gq, policy=pol, ws_bytes=need - 1) == ERR["WS"]
+        assert _call(gq, policy=pol, ws=A + 16) == ERR["ALIGN"]
 
 
 def test_empty_batch_is_noop(gq):

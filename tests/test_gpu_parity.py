@@ -27,7 +27,9 @@ def gq():
 
 def _policies(gq):
     return {
-        "default": None,
+        "default": None,                                           # balanced, v1_max 256
+        "balanced_all_split": gq.policy_default(v1_max_ctx=0),
+        "balanced_no_split": gq.policy_default(v1_max_ctx=1 << 30),
         "pages": gq.policy_pages(),
         "all_split_p32": gq.policy_pages(partition_size=32, v1_max_ctx=0),
         "all_split_p96": gq.policy_pages(partition_size=96, v1_max_ctx=0),
@@ -58,7 +60,7 @@ def test_group_sizes(gq, G):
                         dtype=W.F16)
     ref = R.decode(case)
     dev = case_to_device(case, DEV)
-    for name in ("default", "all_split_p96"):
+    for name in ("default", "balanced_all_split", "all_split_p96"):
         got = run_case(dev, policy=_policies(gq)[name])
         assert_close(got, ref, W.F16, what=f"G={G} {name}")
 
@@ -69,7 +71,7 @@ def test_block_sizes(gq, bs):
                         h_q=8, h_kv=1, d=64, dtype=W.BF16, block_size=bs, extra_blocks=1)
     ref = R.decode(case)
     dev = case_to_device(case, DEV)
-    for name in ("default", "pages", "all_split_p32"):
+    for name in ("default", "balanced_all_split", "pages", "all_split_p32"):
         got = run_case(dev, policy=_policies(gq)[name])
         assert_close(got, ref, W.BF16, what=f"bs={bs} {name}")
 
@@ -147,22 +149,41 @@ def test_paged_bitwise_equals_contiguous(gq):
 def test_deterministic(gq):
     case = W.workload("paged_b64")
     dev = case_to_device(case, DEV)
-    a = run_case(dev, policy=gq.policy_pages(v1_max_ctx=0))
-    for _ in range(2):
-        assert np.array_equal(a, run_case(dev, policy=gq.policy_pages(v1_max_ctx=0)))
+    for pol in (None, gq.policy_pages(v1_max_ctx=0)):
+        a = run_case(dev, policy=pol)
+        for _ in range(2):
+            assert np.array_equal(a, run_case(dev, policy=pol))
 
 
 def test_phases_split_equals_whole(gq):
     case = W.paged_case("ph", 1000, [5000, 100, 9000], h_q=32, h_kv=4, d=128, dtype=W.F16)
     dev = case_to_device(case, DEV)
-    pol = gq.policy_pages()
-    whole = run_case(dev, policy=pol)
-    ws = torch.empty(gq.workspace_size(3, 32, 128, case.max_blocks * 16, pol),
+    for base in (gq.policy_pages(), gq.policy_default()):
+        whole = run_case(dev, policy=base)
+        ws = torch.empty(gq.workspace_size(3, 32, 4, 128, case.max_blocks * 16, base),
+                         dtype=torch.uint8, device=DEV)
+        out = torch.empty_like(dev["q"])
+        p1 = gq.Policy(base.partition_size, base.v1_max_ctx, 1, 0)
+        p2 = gq.Policy(base.partition_size, base.v1_max_ctx, 2, 0)
+        run_case(dev, policy=p1, out=out, workspace=ws)
+        got = run_case(dev, policy=p2, out=out, workspace=ws)
+        assert np.array_equal(whole, got), base
+
+
+def test_reused_workspace_and_changing_lengths(gq):
+    """The same workspace serves consecutive calls whose lengths differ (records are
+    rewritten each call; nothing needs clearing)."""
+    lens_a = [3000, 17, 900, 12000]
+    lens_b = [5, 12000, 300, 1]
+    ca = W.paged_case("wa", 1100, lens_a, h_q=16, h_kv=2, d=128, dtype=W.F16)
+    cb = W.paged_case("wb", 1101, lens_b, h_q=16, h_kv=2, d=128, dtype=W.F16,
+                      max_blocks=ca.max_blocks)
+    pol = gq.policy_default(v1_max_ctx=0)
+    ws = torch.empty(gq.workspace_size(4, 16, 2, 128, ca.max_blocks * 16, pol),
                      dtype=torch.uint8, device=DEV)
-    out = torch.empty_like(dev["q"])
-    run_case(dev, policy=gq.policy_pages(phases=1), out=out, workspace=ws)
-    got = run_case(dev, policy=gq.policy_pages(phases=2), out=out, workspace=ws)
-    assert np.array_equal(whole, got)
+    for c in (ca, cb, ca):
+        got = run_case(case_to_device(c, DEV), policy=pol, workspace=ws)
+        assert_close(got, R.decode(c), W.F16, what=f"reuse {c.name}")
 
 
 def _sample_heads(case, rng, n_seq, per_seq):
@@ -185,7 +206,7 @@ def test_named_workloads_sampled(gq, name):
              if case.kv_bytes <= (1 << 27) else _sample_heads(case, rng, 6, 6))
     ref = R.decode(case, heads=heads)
     dev = case_to_device(case, DEV)
-    for pname in ("default", "pages"):
+    for pname in ("default", "balanced_all_split", "pages"):
         print(f"workload {name} policy={pname} rows={len(heads)}", flush=True)
         got = run_case(dev, policy=_policies(gq)[pname])
         assert np.all(np.isfinite(got)), pname
