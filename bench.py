@@ -1,7 +1,8 @@
 """Benchmark: single-query GQA decode attention on one MI355X.
 
 One step = one pass of the whole decode path (partition kernel + merge kernel)
-over one batch of synthetic inputs already resident in HBM.  K/V are cycled
+over one batch of synthetic inputs already resident in HBM.  The timed steps
+are captured in a HIP graph and replayed between two synchronisations.  K/V are cycled
 over enough device copies (>= 1 GiB in total, i.e. more than four times the
 256 MB Infinity Cache) that no step can be served from the cache a previous
 step filled.
@@ -9,7 +10,8 @@ step filled.
 Prints ONE JSON line.  `value` is K+V GB/s of the headline workload
 (algorithmic K+V bytes / wall time per step between synchronisations);
 `roofline` gives the partition kernel's own HBM roofline fraction, timed with
-HIP events on the launch stream inside the timed region; `cpu_baseline` times
+HIP events on the launch stream around every partition launch of an eager
+pass over the same steps; `cpu_baseline` times
 the float64 oracle on a bounded sample of the same workload; `also` carries
 the other full-size workloads.
 
@@ -45,8 +47,15 @@ def source_hash() -> str:
 
 # ------------------------------------------------------------------ timing --
 
-def time_workload(case, policy_name: str, steps: int, warmup: int, with_events: bool = True):
-    """Time `steps` decode steps of one workload; returns a dict of figures."""
+def time_workload(case, policy_name: str, steps: int, warmup: int):
+    """Time `steps` decode steps of one workload; returns a dict of figures.
+
+    Pass 1 (headline): the `steps` steps captured once in a HIP graph and
+    replayed between two synchronisations, so host launch overhead is not part
+    of the step time.  Pass 2 (kernel roofline): the same steps launched eagerly
+    with HIP events on the launch stream around the partition kernel and the
+    merge kernel of every step.
+    """
     import torch
     import decode_attention_08_amd as gq
     from tests.parity import bits_to_device
@@ -60,90 +69,107 @@ def time_workload(case, policy_name: str, steps: int, warmup: int, with_events: 
     copies = max(2, math.ceil(ROTATE_BYTES / max(1, pool_bytes)))
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
-    if case.layout == "paged":
-        bt = torch.from_numpy(case.block_table).to(dev)
-        ctx = torch.from_numpy(case.ctx_lens).to(dev)
-        call = gq.prepare(q, k0, v0, block_table=bt, ctx_lens=ctx, scale=case.scale, policy=pol)
-    else:
-        call = gq.prepare(q, k0, v0, scale=case.scale, policy=pol)
-    has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.h_kv, case.d,
-                                  (case.max_blocks * case.block_size if case.layout == "paged"
-                                   else case.s_kv), pol) > 0
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        if case.layout == "paged":
+            bt = torch.from_numpy(case.block_table).to(dev)
+            ctx = torch.from_numpy(case.ctx_lens).to(dev)
+            call = gq.prepare(q, k0, v0, block_table=bt, ctx_lens=ctx, scale=case.scale,
+                              policy=pol, stream=stream)
+        else:
+            call = gq.prepare(q, k0, v0, scale=case.scale, policy=pol, stream=stream)
+        max_ctx = case.max_blocks * case.block_size if case.layout == "paged" else case.s_kv
+        has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.h_kv, case.d, max_ctx, pol) > 0
 
-    def step(i, ev=None):
-        k, v = ks[i % copies], vs[i % copies]
-        if ev is None:
-            call(k, v, phases=3)
-            return
-        ev[0].record()
-        call(k, v, phases=1)
-        ev[1].record()
-        if has_merge:
-            call(k, v, phases=2)
-        ev[2].record()
+        for i in range(warmup):
+            call(ks[i % copies], vs[i % copies], phases=3)
+        torch.cuda.synchronize()
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(warmup + i, evs[i] if with_events else None)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
+        # ---- pass 1: graph replay of the timed steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                call(ks[(warmup + i) % copies], vs[(warmup + i) % copies], phases=3)
+        graph.replay()                               # first replay: not timed
+        torch.cuda.synchronize()
+        ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev_a.record(stream)
+        graph.replay()
+        ev_b.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        gpu_step = ev_a.elapsed_time(ev_b) * 1e-3 / steps
+        del graph
+
+        # ---- pass 2: eager steps with events around each kernel
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(steps):
+            kk, vv = ks[(warmup + i) % copies], vs[(warmup + i) % copies]
+            evs[i][0].record(stream)
+            call(kk, vv, phases=1)
+            evs[i][1].record(stream)
+            if has_merge:
+                call(kk, vv, phases=2)
+            evs[i][2].record(stream)
+        torch.cuda.synchronize()
+        eager_wall = (time.perf_counter() - t1) / steps
+    part = sorted(e[0].elapsed_time(e[1]) for e in evs)      # ms
+    merge = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    step_ev = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    mean_part = sum(part) / len(part)
     res = {"workload": case.name, "policy": policy_name,
            "partition_size": pol.partition_size, "v1_max_ctx": pol.v1_max_ctx,
            "kv_bytes": case.kv_bytes, "copies": copies,
            "ms_per_step": wall * 1e3, "us_per_step": wall * 1e6,
-           "gbs": case.kv_bytes / wall / 1e9}
+           "us_per_step_gpu": gpu_step * 1e6,
+           "gbs": case.kv_bytes / wall / 1e9,
+           "eager_us_per_step": eager_wall * 1e6,
+           "partition_us_mean": mean_part * 1e3,
+           "partition_us_median": part[len(part) // 2] * 1e3,
+           "merge_us_mean": sum(merge) / len(merge) * 1e3,
+           "step_us_events_median": step_ev[len(step_ev) // 2] * 1e3,
+           "step_us_events_p10": step_ev[len(step_ev) // 10] * 1e3,
+           "step_us_events_p90": step_ev[(9 * len(step_ev)) // 10] * 1e3,
+           "partition_gbs": case.kv_bytes / (mean_part * 1e-3) / 1e9}
     res["pct_of_peak"] = 100.0 * res["gbs"] / PEAK_GBS
-    if with_events:
-        part = sorted(e[0].elapsed_time(e[1]) for e in evs)      # ms
-        merge = sorted(e[1].elapsed_time(e[2]) for e in evs)
-        step_ev = sorted(e[0].elapsed_time(e[2]) for e in evs)
-        mean_part = sum(part) / len(part)
-        res.update({
-            "partition_us_mean": mean_part * 1e3,
-            "partition_us_median": part[len(part) // 2] * 1e3,
-            "merge_us_mean": sum(merge) / len(merge) * 1e3,
-            "step_us_events_median": step_ev[len(step_ev) // 2] * 1e3,
-            "step_us_events_p10": step_ev[len(step_ev) // 10] * 1e3,
-            "step_us_events_p90": step_ev[(9 * len(step_ev)) // 10] * 1e3,
-            "partition_gbs": case.kv_bytes / (mean_part * 1e-3) / 1e9,
-        })
     del ks, vs
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(case, budget_s: float = 12.0):
-    """The float64 oracle, as it stands, on whole (sequence, KV head) slices of the
-    workload, one BLAS thread; repeated over slices until about budget_s."""
+def cpu_baseline(case, budget_s: float = 10.0):
+    """The float64 oracle, as it stands, over whole (sequence, KV head) slices of the
+    workload in a seeded order, one BLAS thread, repeating passes until about
+    budget_s of CPU time."""
     from threadpoolctl import threadpool_limits
     import numpy as np
     from oracle import reference as R
 
     G = case.h_q // case.h_kv
     pairs = [(s, j) for s in range(case.num_seqs) for j in range(case.h_kv)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(pairs))
+    order = np.random.default_rng(0).permutation(len(pairs))
     done_bytes, done_pairs, t_used = 0, 0, 0.0
     with threadpool_limits(limits=1):
-        for n in order:
-            s, j = pairs[n]
-            heads = [(s, j * G + g) for g in range(G)]
-            t0 = time.perf_counter()
-            R.decode(case, heads=heads)
-            t_used += time.perf_counter() - t0
-            done_bytes += int(case.ctx_lens[s]) * case.d * 2 * 2
-            done_pairs += 1
-            if t_used >= budget_s:
-                break
+        while t_used < budget_s:
+            for n in order:
+                s, j = pairs[n]
+                heads = [(s, j * G + g) for g in range(G)]
+                t0 = time.perf_counter()
+                R.decode(case, heads=heads)
+                t_used += time.perf_counter() - t0
+                done_bytes += int(case.ctx_lens[s]) * case.d * 2 * 2
+                done_pairs += 1
+                if t_used >= budget_s:
+                    break
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{done_pairs} of {len(pairs)} (sequence, KV head) slices of {case.name}, "
-                       f"{done_bytes} K/V bytes in {t_used:.2f} s, float64 numpy, 1 BLAS thread"),
-            "seconds": t_used}
+            "sample": (f"{done_pairs} (sequence, KV head) slices of {case.name} "
+                       f"({len(pairs)} per step, repeated in a seeded order), {done_bytes} K/V "
+                       f"bytes in {t_used:.2f} s; float64 numpy oracle, 1 BLAS thread"),
+            "seconds": round(t_used, 3)}
 
 
 def traffic_for(workload: str, policy: str, kv_bytes: int):
@@ -310,6 +336,9 @@ def main():
                    "kv_copies_rotated": head["copies"]},
         "us_per_step": round(head["us_per_step"], 2),
         "pct_of_peak": round(head["pct_of_peak"], 2),
+        "timing": "graph replay of the timed steps between synchronisations (wall clock); "
+                  "kernel times from an eager pass of the same steps with HIP events",
+        "eager_us_per_step": round(head["eager_us_per_step"], 2),
         "step_us_events": {"median": round(head["step_us_events_median"], 2),
                            "p10": round(head["step_us_events_p10"], 2),
                            "p90": round(head["step_us_events_p90"], 2)},

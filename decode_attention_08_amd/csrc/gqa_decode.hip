@@ -550,18 +550,19 @@ __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_ker
 // order, so the result does not depend on scheduling.
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeGroups = 16;                  // partial subsets per head
+constexpr int kMergeSlices = 8;                   // d slices per head
+constexpr int kMergeGroups = kMergeThreads / kMergeSlices;   // partial subsets per head
 
 template <class DT, int D, bool PAGED, bool BALANCED>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
-  constexpr int E = D / 16;                       // d elements per thread
+  constexpr int E = D / kMergeSlices;             // d elements per thread
   __shared__ __attribute__((aligned(16))) float red_o[kMergeGroups][D];
   __shared__ float red_l[kMergeGroups];
   __shared__ float red_m[kMergeThreads / 64];
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int kg = t / 16;                          // partial subset
-  const int ds = t % 16;                          // d slice
+  const int kg = t / kMergeSlices;                // partial subset
+  const int ds = t % kMergeSlices;                // d slice
   const int heads = a.hpw * a.group;
   const int items = a.num_seqs * a.h_q;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
@@ -599,25 +600,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
     if (lane == 0) red_m[t >> 6] = M;
     __syncthreads();
     M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-    // ---- this thread's subset: partials kg, kg + 16, ...; d in [ds*E, ds*E + E)
+    // ---- this thread's subset: partials kg, kg + G', ...; d in [ds*E, ds*E + E)
     float o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.f;
     float lsum = 0.f;
-    for (int k = kg; k < n; k += kMergeGroups) {
-      const int64_t rw = row(k);
-      const float2 t2 = a.part_ml[rw];
+    auto fold = [&](const float2& t2, const float4_t (&v)[E / 4]) {
       const float wgt = __builtin_amdgcn_exp2f(t2.x - M);
       lsum += wgt * t2.y;
-      const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + ds * E);
 #pragma unroll
-      for (int e4 = 0; e4 < E / 4; ++e4) {
-        const float4_t v = src[e4];
-        o[4 * e4 + 0] += wgt * v[0];
-        o[4 * e4 + 1] += wgt * v[1];
-        o[4 * e4 + 2] += wgt * v[2];
-        o[4 * e4 + 3] += wgt * v[3];
+      for (int e4 = 0; e4 < E / 4; ++e4)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[4 * e4 + c] += wgt * v[e4][c];
+    };
+    int k = kg;
+    for (; k + 3 * kMergeGroups < n; k += 4 * kMergeGroups) {   // four partials in flight
+      float2 t2[4];
+      float4_t v[4][E / 4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t rw = row(k + u * kMergeGroups);
+        t2[u] = a.part_ml[rw];
+        const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + ds * E);
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) v[u][e4] = src[e4];
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fold(t2[u], v[u]);
+    }
+    for (; k < n; k += kMergeGroups) {
+      const int64_t rw = row(k);
+      const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + ds * E);
+      float4_t v[E / 4];
+#pragma unroll
+      for (int e4 = 0; e4 < E / 4; ++e4) v[e4] = src[e4];
+      fold(a.part_ml[rw], v);
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) red_o[kg][ds * E + e] = o[e];
