@@ -217,7 +217,7 @@ def summarize_rocprof(path: str, probe_bytes: int = 1 << 30):
         for n, c, avg, mn, mx, gx, wx, vg, ag, lds in rows:
             lines.append(f"{_short(n):100s} calls={c} avg_ns={avg:.0f} min_ns={mn} max_ns={mx} "
                          f"grid={gx} wg={wx} vgpr={vg} agpr={ag} lds={lds}")
-            if "partition_kernel" in n:
+            if "partition_" in n:
                 rec["partition_avg_ns"] = avg
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         sub = "fetch" if counter == "FETCH_SIZE" else "write"
@@ -235,7 +235,7 @@ def summarize_rocprof(path: str, probe_bytes: int = 1 << 30):
                 lines.append(f"{n:100s} {counter}_KiB avg={sum(vs) / len(vs):.1f} "
                              f"min={min(vs):.1f} max={max(vs):.1f} dispatches={len(vs)}")
             lines.append(f"calibration: 1 GiB probe copy reads {probe} KiB -> factor {factor}")
-            part = [v for n, vs in per.items() if "partition_kernel" in n for v in vs]
+            part = [v for n, vs in per.items() if "partition_" in n for v in vs]
             if part and factor:
                 rec[counter] = {"kib_avg": sum(part) / len(part), "factor": factor,
                                 "bytes_per_launch": sum(part) / len(part) * 1024.0 * factor}
