@@ -545,8 +545,9 @@ __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_ker
 // Persistent grid striding over (sequence, query head).  A head whose sequence
 // was split is merged by the whole workgroup: the n-ary form of the
 // decode-long page's "_merge_running" over its n partials, then its "Final
-// normalise + store".  The 256 threads take 16 interleaved subsets of the
-// partials times 16 slices of d, and the 16 subsets are summed in a fixed
+// normalise + store".  The 256 threads take 32 interleaved subsets of the
+// partials times 8 slices of d; each thread folds its subset in one pass with
+// a running maximum, and the 32 subset results are merged in LDS in a fixed
 // order, so the result does not depend on scheduling.
 
 constexpr int kMergeThreads = 256;
@@ -557,10 +558,9 @@ template <class DT, int D, bool PAGED, bool BALANCED>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
   constexpr int E = D / kMergeSlices;             // d elements per thread
   __shared__ __attribute__((aligned(16))) float red_o[kMergeGroups][D];
+  __shared__ float red_m[kMergeGroups];
   __shared__ float red_l[kMergeGroups];
-  __shared__ float red_m[kMergeThreads / 64];
   const int t = threadIdx.x;
-  const int lane = t & 63;
   const int kg = t / kMergeSlices;                // partial subset
   const int ds = t % kMergeSlices;                // d slice
   const int heads = a.hpw * a.group;
@@ -592,26 +592,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
       else
         return base + k;
     };
-    // ---- M = max_k m_k
-    float M = -INFINITY;
-    for (int k = t; k < n; k += kMergeThreads) M = fmaxf(M, a.part_ml[row(k)].x);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (lane == 0) red_m[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-    // ---- this thread's subset: partials kg, kg + G', ...; d in [ds*E, ds*E + E)
+    // ---- this thread's subset: partials kg, kg + 32, ...; d in [ds*E, ds*E + E).
+    //      Running (m, l, o) in log2 units; a subset with no partial stays (-inf, 0, 0).
+    float m = -INFINITY, l = 0.f;
     float o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.f;
-    float lsum = 0.f;
     auto fold = [&](const float2& t2, const float4_t (&v)[E / 4]) {
-      const float wgt = __builtin_amdgcn_exp2f(t2.x - M);
-      lsum += wgt * t2.y;
+      const float m_new = fmaxf(m, t2.x);         // t2.x is finite: a partial holds a token
+      const float a_old = __builtin_amdgcn_exp2f(m - m_new);
+      const float a_new = __builtin_amdgcn_exp2f(t2.x - m_new);
+      l = l * a_old + t2.y * a_new;
 #pragma unroll
       for (int e4 = 0; e4 < E / 4; ++e4)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[4 * e4 + c] += wgt * v[e4][c];
+        for (int c = 0; c < 4; ++c) o[4 * e4 + c] = o[4 * e4 + c] * a_old + v[e4][c] * a_new;
+      m = m_new;
     };
     int k = kg;
     for (; k + 3 * kMergeGroups < n; k += 4 * kMergeGroups) {   // four partials in flight
@@ -638,16 +634,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) red_o[kg][ds * E + e] = o[e];
-    if (ds == 0) red_l[kg] = lsum;
+    if (ds == 0) {
+      red_m[kg] = m;
+      red_l[kg] = l;
+    }
     __syncthreads();
     if (t < D) {
-      float acc = 0.f, l = 0.f;
+      float M = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) M = fmaxf(M, red_m[g]);
+      float acc = 0.f, lsum = 0.f;
 #pragma unroll
       for (int g = 0; g < kMergeGroups; ++g) {
-        acc += red_o[g][t];
-        l += red_l[g];
+        if (red_m[g] == -INFINITY) continue;      // an empty subset
+        const float w = __builtin_amdgcn_exp2f(red_m[g] - M);
+        acc += w * red_o[g][t];
+        lsum += w * red_l[g];
       }
-      a.out[((int64_t)s * a.h_q + i) * D + t] = static_cast<uint16_t>(DT::narrow(acc / l));
+      a.out[((int64_t)s * a.h_q + i) * D + t] = static_cast<uint16_t>(DT::narrow(acc / lsum));
     }
     __syncthreads();                               // LDS is reused by the next item
   }

@@ -211,3 +211,68 @@ def test_named_workloads_sampled(gq, name):
         got = run_case(dev, policy=_policies(gq)[pname])
         assert np.all(np.isfinite(got)), pname
         assert_close(got, ref, case.dtype, what=f"{name} {pname}")
+
+
+@pytest.mark.parametrize("h_kv,G,d", [(12, 2, 64), (16, 1, 128), (6, 3, 128), (2, 16, 64)])
+def test_head_groups(gq, h_kv, G, d):
+    """KV heads per workgroup = largest divisor of h_kv up to 8 (12 -> 6, 16 -> 8, 6 -> 6)."""
+    case = W.paged_case(f"hg{h_kv}", 1200 + h_kv, [1300, 5, 333], h_q=G * h_kv, h_kv=h_kv, d=d,
+                        dtype=W.BF16, extra_blocks=1)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name in ("default", "balanced_all_split", "pages", "all_split_p96"):
+        got = run_case(dev, policy=_policies(gq)[name])
+        assert_close(got, ref, W.BF16, what=f"h_kv={h_kv} G={G} d={d} {name}")
+
+
+def test_many_sequences_fallback(gq):
+    """More sequences than the balanced scheduler keeps in LDS: fixed 512-token partitions."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 40, size=8200).astype(np.int32)
+    lens[17] = 1500                               # one sequence long enough to split
+    case = W.paged_case("many", 1300, lens, h_q=2, h_kv=1, d=64, dtype=W.F16)
+    heads = [(s, i) for s in list(range(0, 8200, 97)) + [17, 8199] for i in range(2)]
+    ref = R.decode(case, heads=heads)
+    got = run_case(case_to_device(case, DEV))
+    assert_close(got, ref, W.F16, what="8200 sequences")
+
+
+def test_long_sequence_many_segments(gq):
+    """One sequence spread over every workgroup: hundreds of partials per head."""
+    case = W.contiguous_case("long1", 1400, 1, 8, 1, 128, 70001, W.F16)
+    ref = R.decode(case)
+    got = run_case(case_to_device(case, DEV), policy=gq.policy_default(v1_max_ctx=0))
+    assert_close(got, ref, W.F16, what="S=70001")
+    got = run_case(case_to_device(case, DEV), policy=gq.policy_pages(partition_size=64))
+    assert_close(got, ref, W.F16, what="S=70001 fixed 64")
+
+
+@pytest.mark.parametrize("pname", ["default", "pages"])
+def test_graph_replay_matches_eager(gq, pname):
+    """Decode steps captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, equals the eager result bit for bit."""
+    case = W.paged_case("graph", 1500, [3000, 70, 9000, 1], h_q=16, h_kv=4, d=128, dtype=W.F16)
+    dev = case_to_device(case, DEV)
+    pol = _policies(gq)[pname]
+    stream = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(stream):
+        out = torch.empty_like(dev["q"])
+        call = gq.prepare(dev["q"], dev["k"], dev["v"], block_table=dev["block_table"],
+                          ctx_lens=dev["ctx_lens"], scale=case.scale, out=out, policy=pol,
+                          stream=stream)
+        call(phases=3)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            call(phases=3)
+        for rep in range(4):
+            out.zero_()
+            junk = torch.randn(1 << 20, device=DEV).sum()       # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {rep}"
+            del junk
+    assert_close(eager.float().cpu().numpy().astype(np.float64), R.decode(case), W.F16,
+                 what=f"graph {pname}")
