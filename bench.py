@@ -47,6 +47,24 @@ def source_hash() -> str:
 
 # ------------------------------------------------------------------ timing --
 
+_SPIN_RATE = {}
+
+
+def _spin_cycles(torch, stream, seconds: float) -> int:
+    """Cycles of torch.cuda._sleep that keep the stream busy for about `seconds`
+    (rate measured once with events)."""
+    if "rate" not in _SPIN_RATE:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 1 << 20
+        torch.cuda._sleep(n)                       # first launch: not timed
+        a.record(stream)
+        torch.cuda._sleep(n)
+        b.record(stream)
+        torch.cuda.synchronize()
+        _SPIN_RATE["rate"] = n / max(1e-6, a.elapsed_time(b) * 1e-3)   # cycles per second
+    return int(_SPIN_RATE["rate"] * seconds)
+
+
 def time_workload(case, policy_name: str, steps: int, warmup: int):
     """Time `steps` decode steps of one workload; returns a dict of figures.
 
@@ -103,9 +121,13 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
         gpu_step = ev_a.elapsed_time(ev_b) * 1e-3 / steps
         del graph
 
-        # ---- pass 2: eager steps with events around each kernel
+        # ---- pass 2: eager steps with events around each kernel.  A bounded spin
+        # kernel first keeps the stream busy while the host enqueues every launch,
+        # so the events time back-to-back GPU work, not host launch latency.
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        spin = _spin_cycles(torch, stream, seconds=max(2e-3, 400e-6 * steps))
         torch.cuda.synchronize()
+        torch.cuda._sleep(spin)
         t1 = time.perf_counter()
         for i in range(steps):
             kk, vv = ks[(warmup + i) % copies], vs[(warmup + i) % copies]

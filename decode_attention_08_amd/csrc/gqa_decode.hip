@@ -14,10 +14,10 @@
 //                      (kernel-map page, "paged_attention_v2").  Two
 //                      schedulers feed them: fixed partitions (one workgroup
 //                      each) and a balanced persistent grid.
-//   merge kernels      one wave per (sequence, query head) of a split
-//                      sequence: the n-ary form of "_merge_running" over the
-//                      partials, then the decode-long page's "Final
-//                      normalise + store".
+//   merge kernels      1 to 64 slots of 16 lanes per (sequence, query head)
+//                      of a split sequence: the n-ary form of
+//                      "_merge_running" over the partials, then the
+//                      decode-long page's "Final normalise + store".
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_{f16,bf16}, wave64).  The G <= 16
 // query heads of one KV head are the 16-wide N side of both products, padded
@@ -542,118 +542,140 @@ __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_ker
 
 // ----------------------------------------------------------- merge kernel --
 //
-// Persistent grid striding over (sequence, query head).  A head whose sequence
-// was split is merged by the whole workgroup: the n-ary form of the
+// A head whose sequence was split is merged here: the n-ary form of the
 // decode-long page's "_merge_running" over its n partials, then its "Final
-// normalise + store".  The 256 threads take 32 interleaved subsets of the
-// partials times 8 slices of d; each thread folds its subset in one pass with
-// a running maximum, and the 32 subset results are merged in LDS in a fixed
-// order, so the result does not depend on scheduling.
+// normalise + store".  The unit of work is a slot of 16 lanes; lane r of a
+// slot holds d elements [r*D/16, (r+1)*D/16) of one partial row, so a slot
+// reads a whole row per partial with 16-byte loads.  A head gets SPI slots
+// (1, 4, 16 or 64, chosen by the host from the expected number of partials);
+// slot u folds partials u, u + SPI, ... with a running maximum, eight loads
+// in flight, and the SPI slot results are combined in slot order through
+// LDS, so the result does not depend on scheduling.
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeSlices = 8;                   // d slices per head
-constexpr int kMergeGroups = kMergeThreads / kMergeSlices;   // partial subsets per head
+constexpr int kMergeLanes = 16;                   // lanes per slot
+constexpr int kMergeUnroll = 8;                   // partials in flight per slot
 
-template <class DT, int D, bool PAGED, bool BALANCED>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params a) {
-  constexpr int E = D / kMergeSlices;             // d elements per thread
-  __shared__ __attribute__((aligned(16))) float red_o[kMergeGroups][D];
-  __shared__ float red_m[kMergeGroups];
-  __shared__ float red_l[kMergeGroups];
-  const int t = threadIdx.x;
-  const int kg = t / kMergeSlices;                // partial subset
-  const int ds = t % kMergeSlices;                // d slice
+// 256 threads, or one head of SPI slots when that is larger (SPI = 64: 1024)
+__host__ __device__ constexpr int merge_block(int spi) {
+  return spi * kMergeLanes > 256 ? spi * kMergeLanes : 256;
+}
+__host__ __device__ constexpr int merge_heads_per_block(int spi) {
+  return merge_block(spi) / (kMergeLanes * spi);
+}
+
+template <class DT, int D, bool PAGED, bool BALANCED, int SPI>
+__global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
+  constexpr int E = D / kMergeLanes;              // floats per lane: 8 (d = 128) or 4 (d = 64)
+  constexpr int SLOTS = merge_block(SPI) / kMergeLanes;
+  constexpr int HPB = merge_heads_per_block(SPI);
+  static_assert(E % 4 == 0 && HPB >= 1 && HPB * SPI == SLOTS, "merge shape");
+  const int slot = threadIdx.x / kMergeLanes;
+  const int r = threadIdx.x % kMergeLanes;
+  const int sub = slot % SPI;                     // subset of the partials
+  const int item = blockIdx.x * HPB + slot / SPI; // (sequence, query head)
   const int heads = a.hpw * a.group;
-  const int items = a.num_seqs * a.h_q;
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int s = item / a.h_q;
-    const int i = item % a.h_q;
-    // ---- the partial rows of (s, i), or skip a head written in one pass
-    int n;
-    int64_t base = 0;
-    int4 d{0, 0, 0, 0};
+  // ---- the partial rows of this head; n = 0 for a head written in one pass.
+  // No early return: with SPI > 1 every slot reaches the barrier below.
+  int n = 0, s = 0, i = 0;
+  int64_t base = 0;
+  int4 d{0, 0, 0, 0};
+  if (item < a.num_seqs * a.h_q) {
+    s = item / a.h_q;
+    i = item % a.h_q;
     if constexpr (BALANCED) {
       d = a.desc[s * a.n_groups + i / heads];
-      d.x = __builtin_amdgcn_readfirstlane(d.x);
-      d.y = __builtin_amdgcn_readfirstlane(d.y);
-      d.z = __builtin_amdgcn_readfirstlane(d.z);
-      if (d.y == d.x) continue;                   // uniform
-      n = d.y - d.x + 1;
+      n = d.y == d.x ? 0 : d.y - d.x + 1;
     } else {
       const int L = seq_len<PAGED>(a, s);
-      if (L <= a.v1_max_ctx) continue;            // uniform
-      n = (L + a.part_size - 1) / a.part_size;
+      n = L <= a.v1_max_ctx ? 0 : (L + a.part_size - 1) / a.part_size;
       base = ((int64_t)s * a.h_q + i) * a.max_parts;
     }
-    const int local = i % heads;
-    auto row = [&](int k) -> int64_t {
-      if constexpr (BALANCED)
-        return (int64_t)(k == 0 ? d.z : 2 * (d.x + k)) * heads + local;
-      else
-        return base + k;
-    };
-    // ---- this thread's subset: partials kg, kg + 32, ...; d in [ds*E, ds*E + E).
-    //      Running (m, l, o) in log2 units; a subset with no partial stays (-inf, 0, 0).
-    float m = -INFINITY, l = 0.f;
-    float o[E];
+  }
+  const int local = i % heads;
+  auto row = [&](int k) -> int64_t {
+    if constexpr (BALANCED)
+      return (int64_t)(k == 0 ? d.z : 2 * (d.x + k)) * heads + local;
+    else
+      return base + k;
+  };
+  // ---- running (m, l, o) of this slot's subset, log2 units; empty = (-inf, 0, 0)
+  float m = -INFINITY, l = 0.f;
+  float o[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = 0.f;
-    auto fold = [&](const float2& t2, const float4_t (&v)[E / 4]) {
-      const float m_new = fmaxf(m, t2.x);         // t2.x is finite: a partial holds a token
-      const float a_old = __builtin_amdgcn_exp2f(m - m_new);
-      const float a_new = __builtin_amdgcn_exp2f(t2.x - m_new);
-      l = l * a_old + t2.y * a_new;
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  for (int k0 = sub; k0 < n; k0 += kMergeUnroll * SPI) {
+    float2 t2[kMergeUnroll];
+    float4_t v[kMergeUnroll][E / 4];
 #pragma unroll
-      for (int e4 = 0; e4 < E / 4; ++e4)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[4 * e4 + c] = o[4 * e4 + c] * a_old + v[e4][c] * a_new;
-      m = m_new;
-    };
-    int k = kg;
-    for (; k + 3 * kMergeGroups < n; k += 4 * kMergeGroups) {   // four partials in flight
-      float2 t2[4];
-      float4_t v[4][E / 4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t rw = row(k + u * kMergeGroups);
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (k0 + u * SPI < n) {
+        const int64_t rw = row(k0 + u * SPI);
         t2[u] = a.part_ml[rw];
-        const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + ds * E);
+        const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + r * E);
 #pragma unroll
         for (int e4 = 0; e4 < E / 4; ++e4) v[u][e4] = src[e4];
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fold(t2[u], v[u]);
-    }
-    for (; k < n; k += kMergeGroups) {
-      const int64_t rw = row(k);
-      const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + ds * E);
-      float4_t v[E / 4];
-#pragma unroll
-      for (int e4 = 0; e4 < E / 4; ++e4) v[e4] = src[e4];
-      fold(a.part_ml[rw], v);
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) red_o[kg][ds * E + e] = o[e];
-    if (ds == 0) {
-      red_m[kg] = m;
-      red_l[kg] = l;
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (k0 + u * SPI < n) {
+        const float m_new = fmaxf(m, t2[u].x);    // finite: a partial holds at least one token
+        const float a_old = __builtin_amdgcn_exp2f(m - m_new);
+        const float a_new = __builtin_amdgcn_exp2f(t2[u].x - m_new);
+        l = l * a_old + t2[u].y * a_new;
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[4 * e4 + c] = o[4 * e4 + c] * a_old + v[u][e4][c] * a_new;
+        m = m_new;
+      }
+    }
+  }
+  uint16_t* dst = a.out + ((int64_t)s * a.h_q + i) * D;
+  if constexpr (SPI == 1) {
+    if (n > 0) {
+      uint32_t packed[E / 2];
+#pragma unroll
+      for (int e2 = 0; e2 < E / 2; ++e2)
+        packed[e2] = DT::narrow(o[2 * e2] / l) | (DT::narrow(o[2 * e2 + 1] / l) << 16);
+      if constexpr (E == 8)
+        *reinterpret_cast<uint4_t*>(dst + r * E) =
+            uint4_t{packed[0], packed[1], packed[2], packed[3]};
+      else
+        *reinterpret_cast<uint2*>(dst + r * E) = uint2{packed[0], packed[1]};
+    }
+  } else {
+    // ---- combine the SPI slot results of each head in slot order
+    __shared__ float red_o[SLOTS][D];
+    __shared__ float red_m[SLOTS], red_l[SLOTS];
+#pragma unroll
+    for (int e4 = 0; e4 < E / 4; ++e4)
+      *reinterpret_cast<float4_t*>(&red_o[slot][r * E + 4 * e4]) =
+          float4_t{o[4 * e4], o[4 * e4 + 1], o[4 * e4 + 2], o[4 * e4 + 3]};
+    if (r == 0) red_m[slot] = m;
+    __syncthreads();
+    const int first = slot - sub;                 // the head's first slot
+    float sc = 0.f;                               // this slot's weight exp2(m_u - M)
+    if (r == 0 && m != -INFINITY) {               // an empty subset (n < SPI) weighs 0
+      float mm = -INFINITY;
+      for (int u = 0; u < SPI; ++u) mm = fmaxf(mm, red_m[first + u]);
+      sc = __builtin_amdgcn_exp2f(m - mm);
     }
     __syncthreads();
-    if (t < D) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int g = 0; g < kMergeGroups; ++g) M = fmaxf(M, red_m[g]);
-      float acc = 0.f, lsum = 0.f;
-#pragma unroll
-      for (int g = 0; g < kMergeGroups; ++g) {
-        if (red_m[g] == -INFINITY) continue;      // an empty subset
-        const float w = __builtin_amdgcn_exp2f(red_m[g] - M);
-        acc += w * red_o[g][t];
-        lsum += w * red_l[g];
-      }
-      a.out[((int64_t)s * a.h_q + i) * D + t] = static_cast<uint16_t>(DT::narrow(acc / lsum));
+    if (r == 0) {
+      red_m[slot] = sc;
+      red_l[slot] = l * sc;
     }
-    __syncthreads();                               // LDS is reused by the next item
+    __syncthreads();
+    if (n > 0) {
+      float lsum = 0.f;
+      for (int u = 0; u < SPI; ++u) lsum += red_l[first + u];
+      for (int c = sub * kMergeLanes + r; c < D; c += SPI * kMergeLanes) {
+        float acc = 0.f;
+        for (int u = 0; u < SPI; ++u) acc += red_o[first + u][c] * red_m[first + u];
+        dst[c] = DT::narrow(acc / lsum);
+      }
+    }
   }
 }
 
@@ -776,6 +798,37 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds) {
   return grid;
 }
 
+template <int D, bool PAGED>
+size_t balanced_lds(const Params& prm, const Plan& pl) {
+  return (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t) +
+         (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
+}
+
+// Workgroups of the balanced partition launch: the resident count, at most
+// kMaxGrid, and no more than gives every workgroup kMinChunkTiles tiles.
+template <class DT, int D, bool PAGED>
+int balanced_grid(const Params& prm, const Plan& pl) {
+  const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED>);
+  const int resident = resident_grid(kern, 64 * pl.hpw, balanced_lds<D, PAGED>(prm, pl));
+  if (resident <= 0) return 0;
+  const int64_t want =
+      (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxGrid, resident, want}));
+}
+
+template <class DT, int D, bool PAGED, int SPI>
+gqa_status_t launch_merge(bool balanced, int64_t items, void** args, hipStream_t stream) {
+  const void* kern = balanced
+                         ? reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, true, SPI>)
+                         : reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, false, SPI>);
+  constexpr int per_block = merge_heads_per_block(SPI);
+  const int64_t grid = (items + per_block - 1) / per_block;
+  if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(merge_block(SPI)), args, 0, stream) !=
+      hipSuccess)
+    return GQA_ERR_LAUNCH;
+  return GQA_OK;
+}
+
 template <class DT, int D, bool PAGED>
 gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStream_t stream) {
   Params local = prm;
@@ -785,13 +838,10 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
   if (phases & 1) {
     if (pl.balanced) {
       const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED>);
-      const size_t dyn = tiles_lds + (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
-      const int resident = resident_grid(kern, block, dyn);
-      if (resident <= 0) return GQA_ERR_LAUNCH;
-      const int64_t want =
-          (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
-      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxGrid, resident, want}));
-      if (hipLaunchKernel(kern, dim3(grid), dim3(block), args, dyn, stream) != hipSuccess)
+      const int grid = balanced_grid<DT, D, PAGED>(prm, pl);
+      if (grid <= 0) return GQA_ERR_LAUNCH;
+      if (hipLaunchKernel(kern, dim3(grid), dim3(block), args, balanced_lds<D, PAGED>(prm, pl),
+                          stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     } else {
       const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;
@@ -801,14 +851,30 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
     }
   }
   if ((phases & 2) && pl.can_split) {
-    const void* kern = pl.balanced ? reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, true>)
-                                   : reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, false>);
-    const int resident = resident_grid(kern, kMergeThreads, 0);
-    if (resident <= 0) return GQA_ERR_LAUNCH;
+    // partials per split head: about grid / ranges for the balanced scheduler
+    // (a range's tiles spread over that many shares), max_parts for fixed partitions
+    int64_t per_head = pl.max_parts;
+    if (pl.balanced) {
+      const int grid = balanced_grid<DT, D, PAGED>(prm, pl);
+      if (grid <= 0) return GQA_ERR_LAUNCH;
+      const int64_t ranges = std::max<int64_t>(1, (int64_t)prm.num_seqs * pl.n_groups);
+      per_head = (grid + ranges - 1) / ranges + 1;
+    }
     const int64_t items = (int64_t)prm.num_seqs * prm.h_q;
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, resident));
-    if (hipLaunchKernel(kern, dim3(grid), dim3(kMergeThreads), args, 0, stream) != hipSuccess)
-      return GQA_ERR_LAUNCH;
+    // Slots per head: enough that a slot folds at most two batches of partials
+    // and that the launch has 4096 slots or more (1024 waves), at most 16
+    // unless a head has more than 512 partials.
+    int spi = 1;
+    while (spi < 16 && (per_head > 2 * kMergeUnroll * spi || items * spi < 4096)) spi *= 4;
+    if (per_head > 16 * 4 * kMergeUnroll) spi = 64;
+    gqa_status_t st;
+    switch (spi) {
+      case 1: st = launch_merge<DT, D, PAGED, 1>(pl.balanced, items, args, stream); break;
+      case 4: st = launch_merge<DT, D, PAGED, 4>(pl.balanced, items, args, stream); break;
+      case 16: st = launch_merge<DT, D, PAGED, 16>(pl.balanced, items, args, stream); break;
+      default: st = launch_merge<DT, D, PAGED, 64>(pl.balanced, items, args, stream); break;
+    }
+    if (st != GQA_OK) return st;
   }
   return GQA_OK;
 }

@@ -276,3 +276,42 @@ def test_graph_replay_matches_eager(gq, pname):
             del junk
     assert_close(eager.float().cpu().numpy().astype(np.float64), R.decode(case), W.F16,
                  what=f"graph {pname}")
+
+
+def _merge_case(kind):
+    """Fixed 32-token partitions shaped so that the merge runs 1, 4, 16 and 64
+    slots per head: (heads, partials per head) = (4200, 16), (1200, 64), (64, 200), (16, 625)."""
+    rng = np.random.default_rng(1600)
+    if kind == "slots1":
+        lens = rng.integers(0, 513, size=2100)
+        lens[:3] = [512, 0, 33]
+        return W.paged_case(kind, 1601, lens, h_q=2, h_kv=1, d=128, dtype=W.BF16)
+    if kind == "slots4":
+        lens = rng.integers(0, 2049, size=600)
+        lens[:3] = [2048, 1, 65]
+        return W.paged_case(kind, 1602, lens, h_q=2, h_kv=1, d=64, dtype=W.F16)
+    if kind == "slots16":
+        return W.paged_case(kind, 1603, [6400, 3000, 31, 0], h_q=16, h_kv=2, d=128,
+                            dtype=W.BF16, extra_blocks=1)
+    return W.paged_case(kind, 1604, [20000, 777], h_q=8, h_kv=1, d=128, dtype=W.F16)
+
+
+@pytest.mark.parametrize("kind", ["slots1", "slots4", "slots16", "slots64"])
+def test_merge_widths(gq, kind):
+    case = _merge_case(kind)
+    heads = [(s, i) for s in range(min(case.num_seqs, 40)) for i in range(case.h_q)]
+    heads += [(s, 0) for s in range(40, case.num_seqs, 37)]
+    ref = R.decode(case, heads=heads)
+    got = run_case(case_to_device(case, DEV),
+                   policy=gq.policy_pages(partition_size=32, v1_max_ctx=0))
+    assert_close(got, ref, case.dtype, what=f"merge {kind}")
+
+
+@pytest.mark.parametrize("nseq", [1, 4, 16, 64])
+def test_balanced_merge_spread(gq, nseq):
+    """Balanced scheduler, every range split: about grid / nseq partials per head."""
+    case = W.paged_case(f"mwb{nseq}", 1700 + nseq, [9000 - 37 * s for s in range(nseq)],
+                        h_q=32, h_kv=8, d=64, dtype=W.F16)
+    heads = [(s, i) for s in range(min(nseq, 4)) for i in range(32)]
+    got = run_case(case_to_device(case, DEV), policy=gq.policy_default(v1_max_ctx=0))
+    assert_close(got, R.decode(case, heads=heads), W.F16, what=f"balanced nseq={nseq}")
