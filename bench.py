@@ -65,6 +65,27 @@ def _spin_cycles(torch, stream, seconds: float) -> int:
     return int(_SPIN_RATE["rate"] * seconds)
 
 
+XSPLIT_SUFFIX = "_xsplit"
+BENCH_WORKLOADS = ["tiny_contig", "contig_b8", "paged_b64", "long_128k", "mixed_b256",
+                   "paged_b64_xsplit", "mixed_b256_xsplit"]
+
+
+def bench_case(name: str):
+    """A named workload; NAME_xsplit is the paged workload NAME with the same
+    logical cache in the x-split pool layout."""
+    import workloads as W
+    if name.endswith(XSPLIT_SUFFIX):
+        return W.xsplit_case(W.workload(name[:-len(XSPLIT_SUFFIX)]))
+    return W.workload(name)
+
+
+def bench_desc(name: str) -> str:
+    import workloads as W
+    if name.endswith(XSPLIT_SUFFIX):
+        return W.WORKLOADS[name[:-len(XSPLIT_SUFFIX)]][1] + ", x-split pool layout"
+    return W.WORKLOADS[name][1]
+
+
 def time_workload(case, policy_name: str, steps: int, warmup: int):
     """Time `steps` decode steps of one workload; returns a dict of figures.
 
@@ -89,14 +110,14 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(stream):
-        if case.layout == "paged":
+        if case.layout in ("paged", "paged_xsplit"):
             bt = torch.from_numpy(case.block_table).to(dev)
             ctx = torch.from_numpy(case.ctx_lens).to(dev)
             call = gq.prepare(q, k0, v0, block_table=bt, ctx_lens=ctx, scale=case.scale,
-                              policy=pol, stream=stream)
+                              policy=pol, stream=stream, xsplit=case.layout == "paged_xsplit")
         else:
             call = gq.prepare(q, k0, v0, scale=case.scale, policy=pol, stream=stream)
-        max_ctx = case.max_blocks * case.block_size if case.layout == "paged" else case.s_kv
+        max_ctx = case.max_blocks * case.block_size if case.block_table is not None else case.s_kv
         has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.h_kv, case.d, max_ctx, pol) > 0
 
         for i in range(warmup):
@@ -194,18 +215,20 @@ def cpu_baseline(case, budget_s: float = 10.0):
             "seconds": round(t_used, 3)}
 
 
-def traffic_for(workload: str, policy: str, kv_bytes: int):
-    """Measured HBM bytes per partition-kernel launch, if the counters were taken
-    on the current kernel source (else None)."""
+def traffic_for(workload: str, policy: str):
+    """(HBM bytes per partition-kernel launch, rocprofv3 mean kernel duration in
+    us) recorded in profiles/, if taken on the current kernel source, else
+    (None, None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     rec = t.get(f"{workload}/{policy}")
     if not rec or rec.get("source_sha") != source_hash():
-        return None
-    return rec.get("bytes_per_launch")
+        return None, None
+    avg = rec.get("partition_avg_ns")
+    return rec.get("bytes_per_launch"), (None if avg is None else round(avg * 1e-3, 3))
 
 
 # ---------------------------------------------------------------- rocprof --
@@ -308,7 +331,7 @@ def main():
     import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    case = W.workload(args.workload)
+    case = bench_case(args.workload)
     head = time_workload(case, args.policy, args.steps, args.warmup)
     print(f"[bench] {case.name}/{args.policy}: {head['us_per_step']:.1f} us/step wall, "
           f"{head['gbs']:.0f} GB/s, partition {head['partition_us_mean']:.1f} us", file=sys.stderr,
@@ -324,10 +347,12 @@ def main():
 
     also = {}
     if not args.no_also:
-        for name in W.WORKLOADS:
-            c = case if name == args.workload else W.workload(name)
+        for name in BENCH_WORKLOADS:
+            c = case if name == args.workload else bench_case(name)
             for pol in ("default", "pages"):
                 if name == args.workload and pol == args.policy:
+                    continue
+                if name.endswith(XSPLIT_SUFFIX) and pol != "default":
                     continue
                 r = time_workload(c, pol, args.steps, args.warmup)
                 also[f"{name}/{pol}"] = {k: (round(v, 3) if isinstance(v, float) else v)
@@ -338,7 +363,7 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline(case)
     achieved = head["partition_gbs"]
-    traffic = traffic_for(case.name, args.policy, case.kv_bytes)
+    traffic, rocprof_us = traffic_for(case.name, args.policy)
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -352,7 +377,7 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
-        "config": {"workload": case.name, "desc": W.WORKLOADS[case.name][1],
+        "config": {"workload": case.name, "desc": bench_desc(case.name),
                    "policy": args.policy, "partition_size": head["partition_size"],
                    "v1_max_ctx": head["v1_max_ctx"], "kv_bytes": case.kv_bytes,
                    "kv_copies_rotated": head["copies"]},
@@ -368,6 +393,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "partition_kernel",
                      "kernel_us_mean": round(head["partition_us_mean"], 3),
+                     "kernel_us_rocprof": rocprof_us,
                      "merge_us_mean": round(head["merge_us_mean"], 3)},
         "cpu_baseline": cpu,
         "also": also,

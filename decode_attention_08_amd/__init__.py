@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     Policy,
     decode,
     decode_contiguous,
+    decode_xsplit,
+    X,
     lib,
     library_path,
     policy_default,

@@ -20,7 +20,9 @@ GQA_F16 = 0
 GQA_BF16 = 1
 
 EXPORTED_SYMBOLS = ("gqa_policy_default", "gqa_policy_pages", "gqa_decode_workspace_size",
-                    "gqa_decode", "gqa_decode_contiguous", "gqa_status_string")
+                    "gqa_decode", "gqa_decode_xsplit", "gqa_decode_contiguous",
+                    "gqa_status_string")
+X = 8   # elements per 16-byte vector of the x-split K layout
 
 
 class Policy(ctypes.Structure):
@@ -44,6 +46,8 @@ lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
 lib.gqa_decode.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                            _P, ctypes.c_size_t, ctypes.POINTER(Policy), _P]
 lib.gqa_decode.restype = _I
+lib.gqa_decode_xsplit.argtypes = lib.gqa_decode.argtypes
+lib.gqa_decode_xsplit.restype = _I
 lib.gqa_decode_contiguous.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                       _P, ctypes.c_size_t, ctypes.POINTER(Policy), _P]
 lib.gqa_decode_contiguous.restype = _I
@@ -139,14 +143,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     block_table [B, max_blocks] int32, ctx_lens [B] int32 -> out [B, h_q, d]."""
     out = _common(q, {"q": q, "k_cache": k_cache, "v_cache": v_cache,
                       "block_table": block_table, "ctx_lens": ctx_lens}, out)
-    _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "k/v must be [num_blocks, bs, h_kv, d]")
-    _require(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q, k, v must share a dtype")
-    _require(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table: int32 [B, max_blocks]")
-    _require(ctx_lens.dtype == torch.int32 and ctx_lens.dim() == 1, "ctx_lens: int32 [B]")
+    _, bs, h_kv = _paged_shapes(q, k_cache, v_cache, block_table, ctx_lens, False)
     B, h_q, d = q.shape
-    _, bs, h_kv, dk = k_cache.shape
-    _require(dk == d, "head dims differ")
-    _require(block_table.shape[0] == B and ctx_lens.shape[0] == B, "batch sizes differ")
     max_blocks = block_table.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
@@ -154,6 +152,50 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     st = lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
                         _ptr(out), B, max_blocks, h_q, h_kv, d, bs, scale, _dtype_code(q),
                         _ptr(workspace), ws_bytes, _pref(policy), _stream(stream, q.device))
+    if st != 0:
+        raise GqaError(st)
+    return out
+
+
+def _paged_shapes(q, k_cache, v_cache, block_table, ctx_lens, xsplit: bool):
+    """(num_blocks, block_size, h_kv) of a paged cache pair, checked."""
+    _require(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q, k, v must share a dtype")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table: int32 [B, max_blocks]")
+    _require(ctx_lens.dtype == torch.int32 and ctx_lens.dim() == 1, "ctx_lens: int32 [B]")
+    B, h_q, d = q.shape
+    if xsplit:
+        _require(k_cache.dim() == 5 and v_cache.dim() == 4,
+                 "x-split k must be [num_blocks, h_kv, d/8, bs, 8] and v [num_blocks, h_kv, d, bs]")
+        nb, h_kv, dx, bs, x = k_cache.shape
+        _require(x == X and dx * X == d, "x-split k: last dims must be (d/8, bs, 8)")
+        _require(tuple(v_cache.shape) == (nb, h_kv, d, bs), "x-split v must be [num_blocks, h_kv, d, bs]")
+    else:
+        _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "k/v must be [num_blocks, bs, h_kv, d]")
+        nb, bs, h_kv, dk = k_cache.shape
+        _require(dk == d, "head dims differ")
+    _require(block_table.shape[0] == B and ctx_lens.shape[0] == B, "batch sizes differ")
+    return nb, bs, h_kv
+
+
+def decode_xsplit(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_table: torch.Tensor, ctx_lens: torch.Tensor, *,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, policy: Optional[Policy] = None,
+                  stream=None) -> torch.Tensor:
+    """Paged GQA decode over the x-split layout: k [num_blocks, h_kv, d/8, bs, 8],
+    v [num_blocks, h_kv, d, bs]; otherwise as decode()."""
+    out = _common(q, {"q": q, "k_cache": k_cache, "v_cache": v_cache,
+                      "block_table": block_table, "ctx_lens": ctx_lens}, out)
+    _, bs, h_kv = _paged_shapes(q, k_cache, v_cache, block_table, ctx_lens, True)
+    B, h_q, d = q.shape
+    max_blocks = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    st = lib.gqa_decode_xsplit(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                               _ptr(ctx_lens), _ptr(out), B, max_blocks, h_q, h_kv, d, bs, scale,
+                               _dtype_code(q), _ptr(workspace), ws_bytes, _pref(policy),
+                               _stream(stream, q.device))
     if st != 0:
         raise GqaError(st)
     return out
@@ -214,15 +256,17 @@ class PreparedCall:
 
 
 def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
-            workspace=None, policy: Optional[Policy] = None, stream=None) -> PreparedCall:
-    """Validate once (same checks as decode / decode_contiguous) and return a
-    PreparedCall.  Paged when block_table is given, contiguous otherwise."""
+            workspace=None, policy: Optional[Policy] = None, stream=None,
+            xsplit: bool = False) -> PreparedCall:
+    """Validate once (same checks as decode / decode_xsplit / decode_contiguous)
+    and return a PreparedCall.  Paged when block_table is given (x-split layout
+    with xsplit=True), contiguous otherwise."""
     policy = policy_default() if policy is None else policy
     if block_table is not None:
         out = _common(q, {"q": q, "k_cache": k, "v_cache": v, "block_table": block_table,
                           "ctx_lens": ctx_lens}, out)
+        _, bs, h_kv = _paged_shapes(q, k, v, block_table, ctx_lens, xsplit)
         B, h_q, d = q.shape
-        _, bs, h_kv, _ = k.shape
         max_blocks = block_table.shape[1]
         need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
         workspace, ws_bytes = _workspace(workspace, need, q.device)
@@ -230,8 +274,9 @@ def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(ctx_lens), _ptr(out), B,
                 max_blocks, h_q, h_kv, d, bs, scale, _dtype_code(q), _ptr(workspace), ws_bytes,
                 None, _stream(stream, q.device))
-        return PreparedCall(lib.gqa_decode, args, 1, policy,
-                            (q, k, v, block_table, ctx_lens, out, workspace))
+        fn = lib.gqa_decode_xsplit if xsplit else lib.gqa_decode
+        return PreparedCall(fn, args, 1, policy, (q, k, v, block_table, ctx_lens, out, workspace))
+    _require(not xsplit, "the x-split layout is a paged layout (block_table required)")
     out = _common(q, {"q": q, "k": k, "v": v}, out)
     B, h_q, d = q.shape
     _, S, h_kv, _ = k.shape

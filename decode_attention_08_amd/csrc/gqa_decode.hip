@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "gqa_decode.h"
 
@@ -174,9 +175,17 @@ struct Geo {
 // the fp32 partial at pml[g * ml_stride], po[g * o_stride] for head g.  The
 // wave walks its 32-token tiles in order and keeps the next tile's K and V
 // loads in flight while it computes the current one.  vt is the wave's LDS
+// tile (unused with XS).
+//
+// XS selects the x-split paged cache (kernel-map page, "paged_attention_v1",
+// the key_cache layout [num_blocks, h_kv, d / x, block_size, x] with x = 8
+// elements = 16 bytes) with V as [num_blocks, h_kv, d, block_size].  A K
+// load still brings 8 consecutive d of one token; a V load brings 4
+// consecutive tokens of one d, which is already the transposed operand the
+// P.V product needs, so V goes from HBM to the matrix core without the LDS
 // tile.
 
-template <class DT, int D, bool PAGED>
+template <class DT, int D, bool PAGED, bool XS = false>
 __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int s, int j, int t0,
                                              int t1, bool complete, float2* pml,
                                              int64_t ml_stride, float* po, int64_t o_stride) {
@@ -214,10 +223,15 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   const uint32_t tok_stride = (uint32_t)a.h_kv * D;   // elements between consecutive tokens
   const int bs_mask = (1 << a.bs_shift) - 1;
 
-  struct Tile {
+  struct TileRows {
     uint4_t k[2][KK];
     uint4_t v[NIT];
   };
+  struct TileX {
+    uint4_t k[2][KK];
+    uint2 v[NB][2];                               // [d block][half]: 4 tokens of d = 16 nb + col
+  };
+  using Tile = std::conditional_t<XS, TileX, TileRows>;
 
   // Issue every global load of the tile starting at token tb (tb < t1).  Each
   // 16-token half has a wave-uniform base pointer; lanes add small 32-bit
@@ -228,44 +242,81 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
     const uint16_t* kb[2];
     const uint16_t* vb[2];
     int last[2];                                  // last live row of each half
+    if constexpr (XS) {
+      // Each (block, KV head) owns D * block_size contiguous elements in both
+      // caches.  A half past t1 reads the 16-aligned run holding token t1 - 1
+      // instead (same block, in bounds); its weights are zero and its V
+      // elements are cleared in compute().
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int th = min(tb + 16 * hb, t1 - 1);   // 16-aligned unless past t1
-      last[hb] = min(15, t1 - 1 - th);
-      int64_t base;
-      if constexpr (PAGED) {
+      for (int hb = 0; hb < 2; ++hb) {
+        const int th = min(tb + 16 * hb, t1 - 1);
+        last[hb] = min(15, t1 - 1 - th);
         const int32_t blk = load_const(a.block_table, trow + (th >> a.bs_shift));
-        base = ((((int64_t)blk << a.bs_shift) + (th & bs_mask)) * a.h_kv + j) * D;
-      } else {
-        base = (((int64_t)s * a.s_kv + th) * a.h_kv + j) * D;
+        const int64_t region = ((int64_t)blk * a.h_kv + j) * (D << a.bs_shift);
+        kb[hb] = a.k + region + (th & bs_mask) * 8;
+        vb[hb] = a.v + region + (min(tb + 16 * hb, (t1 - 1) & ~15) & bs_mask);
       }
-      kb[hb] = a.k + base;
-      vb[hb] = a.v + base;
-    }
+      // per-lane offsets, computed once; the d-chunk / d-row steps are
+      // wave-uniform and go to the scalar base
+      const uint32_t v_lane = ((uint32_t)col << a.bs_shift) + 4 * grp;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int r = it * RPI + lane / CH;
-      const int hb = r >> 4;                      // uniform per instruction
-      const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
-      T.v[it] = *reinterpret_cast<const uint4_t*>(vb[hb] + off);
-    }
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint32_t k_lane = ((uint32_t)grp << (a.bs_shift + 3)) + min(col, last[hb]) * 8;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint16_t* kbase = kb[hb] + ((int64_t)(kk * 4) << (a.bs_shift + 3));
+          T.k[hb][kk] = *reinterpret_cast<const uint4_t*>(kbase + k_lane);
+        }
+      }
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        T.k[hb][kk] = *reinterpret_cast<const uint4_t*>(kb[hb] + roff + 8 * (kk * 4 + grp));
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const uint16_t* vbase = vb[hb] + ((int64_t)(16 * nb) << a.bs_shift);
+          T.v[nb][hb] = *reinterpret_cast<const uint2*>(vbase + v_lane);
+        }
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int th = min(tb + 16 * hb, t1 - 1);   // 16-aligned unless past t1
+        last[hb] = min(15, t1 - 1 - th);
+        int64_t base;
+        if constexpr (PAGED) {
+          const int32_t blk = load_const(a.block_table, trow + (th >> a.bs_shift));
+          base = ((((int64_t)blk << a.bs_shift) + (th & bs_mask)) * a.h_kv + j) * D;
+        } else {
+          base = (((int64_t)s * a.s_kv + th) * a.h_kv + j) * D;
+        }
+        kb[hb] = a.k + base;
+        vb[hb] = a.v + base;
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + lane / CH;
+        const int hb = r >> 4;                      // uniform per instruction
+        const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
+        T.v[it] = *reinterpret_cast<const uint4_t*>(vb[hb] + off);
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          T.k[hb][kk] = *reinterpret_cast<const uint4_t*>(kb[hb] + roff + 8 * (kk * 4 + grp));
+      }
     }
   };
 
   // fold the tile starting at token tb into (m_run, l_run, acc)
   auto compute = [&](const Tile& T, int tb) {
-    // stage V: row r, chunk c at position c ^ swizzle(r)
+    if constexpr (!XS) {
+      // stage V: row r, chunk c at position c ^ swizzle(r)
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int r = it * RPI + lane / CH;
-      const int pos = (lane % CH) ^ v_swizzle(r);
-      *reinterpret_cast<uint4_t*>(vt + r * D + pos * 8) = T.v[it];
+      for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + lane / CH;
+        const int pos = (lane % CH) ^ v_swizzle(r);
+        *reinterpret_cast<uint4_t*>(vt + r * D + pos * 8) = T.v[it];
+      }
     }
     // scores S^T = K . Q^T
     float4_t sc[2];
@@ -310,25 +361,47 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
     l_run = l_run * alpha + psum;
     const uint4_t phi4{phi[0], phi[1], phi[2], phi[3]};
     const uint4_t plo4{plo[0], plo[1], plo[2], plo[3]};
-    // O^T += V^T . P^T, V^T read transposed from the staged tile
-    wave_lds_fence();
+    if constexpr (XS) {
+      // O^T += V^T . P^T with V^T straight from the loads; in a tile that
+      // reaches past t1, V elements of tokens >= t1 (possibly NaN) are cleared
+      uint2 keep[2] = {make_uint2(~0u, ~0u), make_uint2(~0u, ~0u)};
+      if (tb + kTile > t1) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      uint32_t vv[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int d = 16 * nb + col;
-        const int ra = slot_token(grp, 2 * e2), rb = slot_token(grp, 2 * e2 + 1);
-        const uint32_t lo = vt[ra * D + (((d >> 3) ^ v_swizzle(ra)) << 3) + (d & 7)];
-        const uint32_t hi = vt[rb * D + (((d >> 3) ^ v_swizzle(rb)) << 3) + (d & 7)];
-        vv[e2] = lo | (hi << 16);
+        for (int hb = 0; hb < 2; ++hb) {
+          const int kc = t1 - (tb + 16 * hb + 4 * grp);   // live tokens of the lane's run
+          keep[hb].x = (kc >= 1 ? 0x0000FFFFu : 0u) | (kc >= 2 ? 0xFFFF0000u : 0u);
+          keep[hb].y = (kc >= 3 ? 0x0000FFFFu : 0u) | (kc >= 4 ? 0xFFFF0000u : 0u);
+        }
       }
-      const uint4_t vop{vv[0], vv[1], vv[2], vv[3]};
-      acc[nb] *= alpha;
-      acc[nb] = DT::mfma(vop, phi4, acc[nb]);
-      acc[nb] = DT::mfma(vop, plo4, acc[nb]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4_t vop{T.v[nb][0].x & keep[0].x, T.v[nb][0].y & keep[0].y,
+                          T.v[nb][1].x & keep[1].x, T.v[nb][1].y & keep[1].y};
+        acc[nb] *= alpha;
+        acc[nb] = DT::mfma(vop, phi4, acc[nb]);
+        acc[nb] = DT::mfma(vop, plo4, acc[nb]);
+      }
+    } else {
+      // O^T += V^T . P^T, V^T read transposed from the staged tile
+      wave_lds_fence();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t vv[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int d = 16 * nb + col;
+          const int ra = slot_token(grp, 2 * e2), rb = slot_token(grp, 2 * e2 + 1);
+          const uint32_t lo = vt[ra * D + (((d >> 3) ^ v_swizzle(ra)) << 3) + (d & 7)];
+          const uint32_t hi = vt[rb * D + (((d >> 3) ^ v_swizzle(rb)) << 3) + (d & 7)];
+          vv[e2] = lo | (hi << 16);
+        }
+        const uint4_t vop{vv[0], vv[1], vv[2], vv[3]};
+        acc[nb] *= alpha;
+        acc[nb] = DT::mfma(vop, phi4, acc[nb]);
+        acc[nb] = DT::mfma(vop, plo4, acc[nb]);
+      }
+      wave_lds_fence();                               // reads retire before the next stores
     }
-    wave_lds_fence();                               // reads retire before the next stores
   };
 
   // ---- token loop: two register tiles ping-ponged so that the next tile's
@@ -395,7 +468,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
 // most v1_max_ctx tokens is one partition written directly, a longer one is
 // cut into ceil(L / part_size) partitions whose partials land at [s, i, p].
 
-template <class DT, int D, bool PAGED>
+template <class DT, int D, bool PAGED, bool XS>
 __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_fixed_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -411,7 +484,7 @@ __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_fixed_kernel
   const int t1 = split ? min(t0 + a.part_size, L) : L;
   const int j = hg * a.hpw + w;
   const int64_t row0 = (int64_t)s * a.h_q + j * a.group;
-  wave_segment<DT, D, PAGED>(a, smem + w * Geo<D>::V_TILE, s, j, t0, t1, !split,
+  wave_segment<DT, D, PAGED, XS>(a, smem + (XS ? 0 : w * Geo<D>::V_TILE), s, j, t0, t1, !split,
                              a.part_ml + row0 * a.max_parts + p, a.max_parts,
                              a.part_o + (row0 * a.max_parts + p) * D, (int64_t)a.max_parts * D);
 }
@@ -441,15 +514,16 @@ __device__ __forceinline__ int64_t range_prefix(const Params& a, const int32_t* 
     return (int64_t)s * a.n_groups * seq_tiles(a.s_kv);
 }
 
-template <class DT, int D, bool PAGED>
+template <class DT, int D, bool PAGED, bool XS>
 __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles, then the prefix
   __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;                // = hpw
-  uint16_t* const vt = smem + w * Geo<D>::V_TILE;
-  int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * Geo<D>::V_TILE);
+  constexpr int VT = XS ? 0 : Geo<D>::V_TILE;     // the x-split layout stages nothing
+  uint16_t* const vt = smem + w * VT;
+  int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * VT);
 
   // ---- paged: pref[s] = n_groups * (tiles of sequences < s); arithmetic when contiguous
   int64_t total;
@@ -511,7 +585,7 @@ __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_ker
     const int j = hg * a.hpw + w;
     if (L <= a.v1_max_ctx) {
       if (rs >= x0) {                            // owned: the whole range, never split
-        wave_segment<DT, D, PAGED>(a, vt, s, j, 0, L, true, nullptr, 0, nullptr, 0);
+        wave_segment<DT, D, PAGED, XS>(a, vt, s, j, 0, L, true, nullptr, 0, nullptr, 0);
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       }
     } else {
@@ -520,12 +594,12 @@ __global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_ker
       const int t0 = (int)(sa * kTile);
       const int t1 = (int)min(sb * kTile, (int64_t)L);
       if (sa == 0 && sb == nt) {
-        wave_segment<DT, D, PAGED>(a, vt, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
+        wave_segment<DT, D, PAGED, XS>(a, vt, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       } else {
         const int slot = 2 * wg + (rs <= x0 ? 0 : 1);
         const int64_t hrow = (int64_t)slot * heads + w * a.group;
-        wave_segment<DT, D, PAGED>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
+        wave_segment<DT, D, PAGED, XS>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
                                    a.part_o + hrow * D, D);
         if (sa == 0 && threadIdx.x == 0)
           a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
@@ -686,6 +760,7 @@ constexpr int32_t kFallbackPartition = 512;
 
 struct Problem {
   bool paged;
+  bool xsplit;        // paged caches in the x-split layout
   const void* q;
   const void* k;
   const void* v;
@@ -798,18 +873,18 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds) {
   return grid;
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool XS>
 size_t balanced_lds(const Params& prm, const Plan& pl) {
-  return (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t) +
+  return (XS ? 0 : (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t)) +
          (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
 }
 
 // Workgroups of the balanced partition launch: the resident count, at most
 // kMaxGrid, and no more than gives every workgroup kMinChunkTiles tiles.
-template <class DT, int D, bool PAGED>
+template <class DT, int D, bool PAGED, bool XS>
 int balanced_grid(const Params& prm, const Plan& pl) {
-  const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED>);
-  const int resident = resident_grid(kern, 64 * pl.hpw, balanced_lds<D, PAGED>(prm, pl));
+  const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS>);
+  const int resident = resident_grid(kern, 64 * pl.hpw, balanced_lds<D, PAGED, XS>(prm, pl));
   if (resident <= 0) return 0;
   const int64_t want =
       (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
@@ -829,23 +904,24 @@ gqa_status_t launch_merge(bool balanced, int64_t items, void** args, hipStream_t
   return GQA_OK;
 }
 
-template <class DT, int D, bool PAGED>
+template <class DT, int D, bool PAGED, bool XS>
 gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStream_t stream) {
   Params local = prm;
   void* args[] = {&local};
   const int block = 64 * pl.hpw;
-  const size_t tiles_lds = (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t);
+  const size_t tiles_lds = XS ? 0 : (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t);
   if (phases & 1) {
     if (pl.balanced) {
-      const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED>);
-      const int grid = balanced_grid<DT, D, PAGED>(prm, pl);
+      const void* kern =
+          reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS>);
+      const int grid = balanced_grid<DT, D, PAGED, XS>(prm, pl);
       if (grid <= 0) return GQA_ERR_LAUNCH;
-      if (hipLaunchKernel(kern, dim3(grid), dim3(block), args, balanced_lds<D, PAGED>(prm, pl),
-                          stream) != hipSuccess)
+      if (hipLaunchKernel(kern, dim3(grid), dim3(block), args,
+                          balanced_lds<D, PAGED, XS>(prm, pl), stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     } else {
       const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;
-      if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED>),
+      if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS>),
                           dim3((unsigned)grid), dim3(block), args, tiles_lds, stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     }
@@ -855,7 +931,7 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
     // (a range's tiles spread over that many shares), max_parts for fixed partitions
     int64_t per_head = pl.max_parts;
     if (pl.balanced) {
-      const int grid = balanced_grid<DT, D, PAGED>(prm, pl);
+      const int grid = balanced_grid<DT, D, PAGED, XS>(prm, pl);
       if (grid <= 0) return GQA_ERR_LAUNCH;
       const int64_t ranges = std::max<int64_t>(1, (int64_t)prm.num_seqs * pl.n_groups);
       per_head = (grid + ranges - 1) / ranges + 1;
@@ -879,14 +955,19 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
   return GQA_OK;
 }
 
+template <class DT, int D>
+gqa_status_t launch_layout(const Problem& pb, const Params& prm, const Plan& pl, int ph,
+                           hipStream_t st) {
+  if (pb.xsplit) return launch_typed<DT, D, true, true>(prm, pl, ph, st);
+  return pb.paged ? launch_typed<DT, D, true, false>(prm, pl, ph, st)
+                  : launch_typed<DT, D, false, false>(prm, pl, ph, st);
+}
+
 template <class DT>
 gqa_status_t launch_dtype(const Problem& pb, const Params& prm, const Plan& pl, int ph,
                           hipStream_t st) {
-  if (pb.d == 64)
-    return pb.paged ? launch_typed<DT, 64, true>(prm, pl, ph, st)
-                    : launch_typed<DT, 64, false>(prm, pl, ph, st);
-  return pb.paged ? launch_typed<DT, 128, true>(prm, pl, ph, st)
-                  : launch_typed<DT, 128, false>(prm, pl, ph, st);
+  return pb.d == 64 ? launch_layout<DT, 64>(pb, prm, pl, ph, st)
+                    : launch_layout<DT, 128>(pb, prm, pl, ph, st);
 }
 
 gqa_status_t run(const Problem& pb) {
@@ -965,6 +1046,35 @@ gqa_status_t run(const Problem& pb) {
   return launch_dtype<BF16>(pb, prm, pl, pol.phases, st);
 }
 
+gqa_status_t run_paged(bool xsplit, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* ctx_lens, void* out,
+                       int num_seqs, int max_blocks_per_seq, int h_q, int h_kv, int d_head,
+                       int block_size, float scale, gqa_dtype_t dtype, void* workspace,
+                       size_t workspace_bytes, const gqa_policy_t* policy, void* stream) {
+  Problem pb{};
+  pb.paged = true;
+  pb.xsplit = xsplit;
+  pb.q = q;
+  pb.k = k_cache;
+  pb.v = v_cache;
+  pb.out = out;
+  pb.block_table = block_table;
+  pb.ctx_lens = ctx_lens;
+  pb.num_seqs = num_seqs;
+  pb.max_blocks = max_blocks_per_seq;
+  pb.h_q = h_q;
+  pb.h_kv = h_kv;
+  pb.d = d_head;
+  pb.block_size = block_size;
+  pb.scale = scale;
+  pb.dtype = dtype;
+  pb.ws = workspace;
+  pb.ws_bytes = workspace_bytes;
+  pb.policy = policy;
+  pb.stream = stream;
+  return run(pb);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1000,27 +1110,20 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                         int d_head, int block_size, float scale, gqa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes,
                         const gqa_policy_t* policy, void* stream) {
-  Problem pb{};
-  pb.paged = true;
-  pb.q = q;
-  pb.k = k_cache;
-  pb.v = v_cache;
-  pb.out = out;
-  pb.block_table = block_table;
-  pb.ctx_lens = ctx_lens;
-  pb.num_seqs = num_seqs;
-  pb.max_blocks = max_blocks_per_seq;
-  pb.h_q = h_q;
-  pb.h_kv = h_kv;
-  pb.d = d_head;
-  pb.block_size = block_size;
-  pb.scale = scale;
-  pb.dtype = dtype;
-  pb.ws = workspace;
-  pb.ws_bytes = workspace_bytes;
-  pb.policy = policy;
-  pb.stream = stream;
-  return run(pb);
+  return run_paged(false, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
+                   max_blocks_per_seq, h_q, h_kv, d_head, block_size, scale, dtype, workspace,
+                   workspace_bytes, policy, stream);
+}
+
+gqa_status_t gqa_decode_xsplit(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_lens, void* out,
+                               int num_seqs, int max_blocks_per_seq, int h_q, int h_kv,
+                               int d_head, int block_size, float scale, gqa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes,
+                               const gqa_policy_t* policy, void* stream) {
+  return run_paged(true, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
+                   max_blocks_per_seq, h_q, h_kv, d_head, block_size, scale, dtype, workspace,
+                   workspace_bytes, policy, stream);
 }
 
 gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, void* out,

@@ -24,6 +24,7 @@
  * Layouts (row-major, contiguous, 16-byte aligned base pointers):
  *   q, out          [num_seqs, h_q, d_head]                    dtype
  *   paged k, v      [num_blocks, block_size, h_kv, d_head]     dtype
+ *                   (gqa_decode_xsplit: the x-split layout given there)
  *   contiguous k, v [num_seqs, s_kv, h_kv, d_head]             dtype
  *   block_table     [num_seqs, max_blocks_per_seq]             int32
  *   ctx_lens        [num_seqs]                                 int32
@@ -140,6 +141,27 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                         int d_head, int block_size, float scale, gqa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes,
                         const gqa_policy_t* policy, void* stream);
+
+/*
+ * Paged decode over the x-split cache layout (kernel-map page,
+ * VLLM_KERNEL_MAP "paged_attention_v1": key_cache
+ * [num_blocks, num_kv_heads, head_dim // x, block_size, x]):
+ *   k_cache   [num_blocks, h_kv, d_head / 8, block_size, 8]   dtype
+ *   v_cache   [num_blocks, h_kv, d_head, block_size]          dtype
+ * x = 8 elements (16 bytes of fp16/bf16): element d of token slot o of KV
+ * head j in block b is k_cache[b, j, d / 8, o, d % 8] and v_cache[b, j, d, o].
+ * The page gives no V layout; V keeps the tokens of one d consecutive, the
+ * axis the P.V product sums over, as K keeps the d of one token consecutive.
+ * Everything else (arguments, block_table, ctx_lens, workspace, policy,
+ * errors) is as for gqa_decode, and both give bit-identical outputs on the
+ * same logical cache.
+ */
+gqa_status_t gqa_decode_xsplit(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_lens, void* out,
+                               int num_seqs, int max_blocks_per_seq, int h_q, int h_kv,
+                               int d_head, int block_size, float scale, gqa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes,
+                               const gqa_policy_t* policy, void* stream);
 
 /*
  * Contiguous decode: every sequence holds s_kv tokens (s_kv >= 0) in a

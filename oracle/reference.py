@@ -76,11 +76,37 @@ def gather_paged(k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray
     return np.stack(rows_k), np.stack(rows_v)
 
 
+def gather_paged_xsplit(k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray,
+                        s: int, j: int, L: int, block_size: int):
+    """K_s, V_s for logical tokens t < L of an x-split pool.
+
+    Kernel-map page, ``paged_attention_v1``: the key cache is
+    [num_blocks, num_kv_heads, head_dim // x, block_size, x], so element d of
+    the token in slot o of block b is k_pool[b, j, d // x, o, d % x] (x is the
+    pool's last extent).  The page gives no value-cache layout; the reading
+    used here is [num_blocks, num_kv_heads, head_dim, block_size], element
+    v_pool[b, j, d, o].
+    """
+    x = k_pool.shape[-1]
+    d = k_pool.shape[2] * x
+    K = np.zeros((L, d), dtype=k_pool.dtype)
+    V = np.zeros((L, d), dtype=v_pool.dtype)
+    for t in range(L):
+        b = int(block_table[s, t // block_size])
+        o = t % block_size
+        # the [d // x, d % x] slice read in C order is d = (d // x) * x + d % x
+        K[t, :] = k_pool[b, j, :, o, :].reshape(d)
+        V[t, :] = v_pool[b, j, :, o]
+    return K, V
+
+
 def sequence_kv(case, s: int, j: int):
     """Float64 K_s, V_s of (sequence s, KV head j) for a workloads.DecodeCase."""
     L = int(case.ctx_lens[s])
     if case.layout == "contiguous":
         K, V = gather_contiguous(case.k, case.v, s, j, L)
+    elif case.layout == "paged_xsplit":
+        K, V = gather_paged_xsplit(case.k, case.v, case.block_table, s, j, L, case.block_size)
     else:
         K, V = gather_paged(case.k, case.v, case.block_table, s, j, L, case.block_size)
     return upcast(K, case.dtype), upcast(V, case.dtype)

@@ -28,7 +28,7 @@ def case_to_device(case, device, copies: int = 1):
     dev = {"case": case, "q": bits_to_device(case.q, case.dtype, device)}
     dev["k"] = bits_to_device(case.k, case.dtype, device)
     dev["v"] = bits_to_device(case.v, case.dtype, device)
-    if case.layout == "paged":
+    if case.layout in ("paged", "paged_xsplit"):
         dev["block_table"] = torch.from_numpy(case.block_table).to(device)
         dev["ctx_lens"] = torch.from_numpy(case.ctx_lens).to(device)
     return dev
@@ -43,6 +43,9 @@ def run_case(dev, policy=None, out=None, workspace=None, k=None, v=None) -> np.n
     if case.layout == "paged":
         res = gq.decode(dev["q"], k, v, dev["block_table"], dev["ctx_lens"], scale=case.scale,
                         out=out, workspace=workspace, policy=policy)
+    elif case.layout == "paged_xsplit":
+        res = gq.decode_xsplit(dev["q"], k, v, dev["block_table"], dev["ctx_lens"],
+                               scale=case.scale, out=out, workspace=workspace, policy=policy)
     else:
         res = gq.decode_contiguous(dev["q"], k, v, scale=case.scale, out=out,
                                    workspace=workspace, policy=policy)

@@ -81,12 +81,12 @@ B = 0x20000
 MIS = 0x10008
 
 
-def _call(gq, **kw):
+def _call(gq, entry="gqa_decode", **kw):
     a = dict(q=A, k=A, v=A, bt=A, ctx=A, out=B, num_seqs=2, max_blocks=4, h_q=8, h_kv=2,
              d=128, bs=16, scale=0.1, dtype=0, ws=A, ws_bytes=1 << 30, policy=None)
     a.update(kw)
     pol = None if a["policy"] is None else ctypes.byref(a["policy"])
-    return gq.lib.gqa_decode(a["q"], a["k"], a["v"], a["bt"], a["ctx"], a["out"], a["num_seqs"],
+    return getattr(gq.lib, entry)(a["q"], a["k"], a["v"], a["bt"], a["ctx"], a["out"], a["num_seqs"],
                              a["max_blocks"], a["h_q"], a["h_kv"], a["d"], a["bs"], a["scale"],
                              a["dtype"], a["ws"], a["ws_bytes"], pol, None)
 
@@ -118,8 +118,9 @@ ERR = dict(NULL=1, SHAPE=2, UNSUP=3, ALIGN=4, WS=5, POLICY=6, SCALE=7)
     (dict(out=MIS), "ALIGN"),
     (dict(ctx=A + 2), "ALIGN"),
 ])
-def test_validation_errors(gq, kw, code):
-    assert _call(gq, **kw) == ERR[code]
+@pytest.mark.parametrize("entry", ["gqa_decode", "gqa_decode_xsplit"])
+def test_validation_errors(gq, kw, code, entry):
+    assert _call(gq, entry, **kw) == ERR[code]
 
 
 def test_policy_and_workspace_errors(gq):
@@ -127,6 +128,7 @@ def test_policy_and_workspace_errors(gq):
                 gq.Policy(512, -1, 0, 0), gq.Policy(0, -1, 0, 0), gq.Policy(512, 0, 4, 0),
                 gq.Policy(0, 0, -1, 0), gq.Policy(512, 0, 0, 1), gq.Policy(1 << 21, 0, 0, 0)):
         assert _call(gq, policy=pol) == ERR["POLICY"], pol
+        assert _call(gq, "gqa_decode_xsplit", policy=pol) == ERR["POLICY"], pol
     for pol in (gq.policy_pages(v1_max_ctx=0), gq.policy_default(v1_max_ctx=0)):
         need = gq.workspace_size(2, 8, 2, 128, 64, pol)           # everything may split
         assert need > 0

@@ -1,0 +1,107 @@
+"""GPU parity of the x-split paged cache layout (gqa_decode_xsplit).
+
+The x-split pools hold the same logical cache as the row-layout pools of the
+same seed (workloads.xsplit_case), so the library must give bit-identical
+outputs through either entry point, and match the float64 oracle (which
+gathers the x-split pools by the layout's own indexing) within the tolerance
+in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import reference as R
+from tests.parity import assert_close, case_to_device, run_case
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import decode_attention_08_amd as m
+    return m
+
+
+def _policies(gq):
+    return {
+        "default": None,
+        "balanced_all_split": gq.policy_default(v1_max_ctx=0),
+        "pages": gq.policy_pages(),
+        "all_split_p32": gq.policy_pages(partition_size=32, v1_max_ctx=0),
+        "all_split_p96": gq.policy_pages(partition_size=96, v1_max_ctx=0),
+    }
+
+
+EDGE_LENGTHS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 511, 512, 513, 1000, 8193]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_xsplit_edge_lengths(gq, dtype, d):
+    rows = W.paged_case(f"xe_{dtype}_{d}", 2000 + d, EDGE_LENGTHS, h_q=16, h_kv=2, d=d,
+                        dtype=dtype, extra_blocks=3)
+    xs = W.xsplit_case(rows)
+    ref = R.decode(xs)
+    dev_r, dev_x = case_to_device(rows, DEV), case_to_device(xs, DEV)
+    for name, pol in _policies(gq).items():
+        print(f"xsplit edges dtype={dtype} d={d} policy={name}", flush=True)
+        got_x = run_case(dev_x, policy=pol)
+        got_r = run_case(dev_r, policy=pol)
+        assert np.array_equal(got_x, got_r), f"x-split differs from rows ({name})"
+        assert_close(got_x, ref, dtype, what=f"xsplit edges {dtype} d={d} {name}")
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+def test_xsplit_block_sizes(gq, bs):
+    rows = W.paged_case(f"xbs{bs}", 2100 + bs, [1, bs - 1, bs, bs + 1, 3 * bs + 5, 700],
+                        h_q=8, h_kv=1, d=128, dtype=W.F16, block_size=bs, extra_blocks=1)
+    xs = W.xsplit_case(rows)
+    ref = R.decode(xs)
+    dev_r, dev_x = case_to_device(rows, DEV), case_to_device(xs, DEV)
+    for name in ("default", "balanced_all_split", "all_split_p32"):
+        pol = _policies(gq)[name]
+        got_x = run_case(dev_x, policy=pol)
+        assert np.array_equal(got_x, run_case(dev_r, policy=pol)), name
+        assert_close(got_x, ref, W.F16, what=f"xsplit bs={bs} {name}")
+
+
+@pytest.mark.parametrize("h_kv,G", [(1, 1), (2, 3), (8, 4), (6, 2), (2, 16)])
+def test_xsplit_groups(gq, h_kv, G):
+    rows = W.paged_case(f"xg{h_kv}_{G}", 2200 + 10 * h_kv + G, [1300, 5, 333, 64],
+                        h_q=G * h_kv, h_kv=h_kv, d=64, dtype=W.BF16, extra_blocks=1)
+    xs = W.xsplit_case(rows)
+    ref = R.decode(xs)
+    got = run_case(case_to_device(xs, DEV))
+    assert_close(got, ref, W.BF16, what=f"xsplit h_kv={h_kv} G={G}")
+
+
+@pytest.mark.parametrize("name", ["paged_b64", "mixed_b256"])
+def test_xsplit_named_workloads_sampled(gq, name):
+    rows = W.workload(name)
+    xs = W.xsplit_case(rows)
+    del rows
+    rng = np.random.default_rng(4321)
+    longest = int(np.argmax(xs.ctx_lens))
+    seqs = sorted(set(rng.choice(xs.num_seqs, size=5, replace=False).tolist() + [longest]))
+    heads = [(s, i) for s in seqs for i in rng.choice(xs.h_q, size=4, replace=False)]
+    ref = R.decode(xs, heads=heads)
+    dev = case_to_device(xs, DEV)
+    for pname in ("default", "pages"):
+        print(f"xsplit workload {name} policy={pname}", flush=True)
+        got = run_case(dev, policy=_policies(gq)[pname])
+        assert np.all(np.isfinite(got)), pname
+        assert_close(got, ref, xs.dtype, what=f"xsplit {name} {pname}")
+
+
+def test_xsplit_shape_checks(gq):
+    rows = W.paged_case("xchk", 2300, [40], h_q=4, h_kv=2, d=64, dtype=W.F16)
+    xs = W.xsplit_case(rows)
+    dev_r, dev_x = case_to_device(rows, DEV), case_to_device(xs, DEV)
+    with pytest.raises(ValueError):
+        gq.decode_xsplit(dev_x["q"], dev_r["k"], dev_r["v"], dev_x["block_table"],
+                         dev_x["ctx_lens"])
+    with pytest.raises(ValueError):
+        gq.decode(dev_r["q"], dev_x["k"], dev_x["v"], dev_r["block_table"], dev_r["ctx_lens"])

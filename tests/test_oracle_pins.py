@@ -286,6 +286,45 @@ def pin_paged_equals_contiguous():
     assert np.array_equal(a, b)
 
 
+def pin_xsplit_gather_coded():
+    """x-split pools whose every element holds its own (block, head, d, slot)
+    code, laid out as the kernel-map page's key cache
+    [num_blocks, h_kv, d / x, block_size, x] (and V as [num_blocks, h_kv, d,
+    block_size]): the gather must return code(table[s, t // bs], j, d, t % bs)."""
+    nb, h_kv, d, bs, x = 3, 2, 16, 16, 8
+
+    def code(b, j, dd, o):
+        return ((b * h_kv + j) * d + dd) * bs + o
+
+    k = np.zeros((nb, h_kv, d // x, bs, x), np.int64)
+    v = np.zeros((nb, h_kv, d, bs), np.int64)
+    for b in range(nb):
+        for j in range(h_kv):
+            for dd in range(d):
+                for o in range(bs):
+                    k[b, j, dd // x, o, dd % x] = code(b, j, dd, o)
+                    v[b, j, dd, o] = code(b, j, dd, o) + 7
+    table = np.array([[2, 0, -1], [1, -1, -1]], np.int32)
+    for s, L in ((0, 20), (1, 16)):
+        for j in range(h_kv):
+            K, V = R.gather_paged_xsplit(k, v, table, s, j, L, bs)
+            assert K.shape == (L, d) and V.shape == (L, d)
+            for t in range(L):
+                for dd in range(d):
+                    want = code(int(table[s, t // bs]), j, dd, t % bs)
+                    assert K[t, dd] == want and V[t, dd] == want + 7, (s, j, t, dd)
+
+
+def pin_xsplit_equals_rows():
+    """The same logical cache in the x-split layout decodes bit-identically."""
+    rows = W.paged_case("xr", 43, [33, 16, 1, 50, 0], h_q=8, h_kv=2, d=16, dtype=W.BF16,
+                        block_size=16, extra_blocks=2)
+    xs = W.xsplit_case(rows)
+    a, b = R.decode(rows), R.decode(xs)
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b)
+
+
 def pin_empty_sequence_zero():
     case = W.paged_case("e", 41, [0, 3], h_q=2, h_kv=1, d=4, dtype=W.F16, block_size=16)
     out = R.decode(case)
@@ -318,7 +357,8 @@ PINS = [pin_upcast_known_bits, pin_golden_closed_form, pin_brute_force_tiny, pin
         pin_single_token, pin_zero_query_mean, pin_identical_keys_mean,
         pin_weights_simplex, pin_two_token_closed_form, pin_invariances,
         pin_merge_split, pin_stability_and_argmax_limit, pin_sdpa_library_routine,
-        pin_paged_equals_contiguous, pin_empty_sequence_zero]
+        pin_paged_equals_contiguous, pin_xsplit_gather_coded, pin_xsplit_equals_rows,
+        pin_empty_sequence_zero]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -338,6 +378,18 @@ def _m_transposed_slot(k_pool, v_pool, block_table, s, j, L, block_size):
     rows_v = [v_pool[int(block_table[s, t % block_size]) if t % block_size < block_table.shape[1] else 0,
                      t // block_size, j, :] for t in range(L)]
     return np.stack(rows_k), np.stack(rows_v)
+
+
+def _m_xsplit_chunks_transposed(k_pool, v_pool, block_table, s, j, L, block_size):
+    x = k_pool.shape[-1]
+    d = k_pool.shape[2] * x
+    K = np.zeros((L, d), dtype=k_pool.dtype)
+    V = np.zeros((L, d), dtype=v_pool.dtype)
+    for t in range(L):
+        b = int(block_table[s, t // block_size])
+        K[t, :] = k_pool[b, j, :, t % block_size, :].T.reshape(d)
+        V[t, :] = v_pool[b, j, :, t % block_size]
+    return K, V
 
 
 def _m_kv_interleaved(i, group):
@@ -396,6 +448,7 @@ _ORIG_PARTIAL = R.partial
 MUTANTS = {
     "logits_without_scale": ("logits", _m_no_scale),
     "paged_block_and_slot_swapped": ("gather_paged", _m_transposed_slot),
+    "xsplit_chunks_transposed": ("gather_paged_xsplit", _m_xsplit_chunks_transposed),
     "kv_head_interleaved": ("kv_head", _m_kv_interleaved),
     "softmax_without_max_shift": ("softmax", _m_softmax_no_max),
     "softmax_unnormalised": ("softmax", _m_softmax_unnormalised),

@@ -11,6 +11,8 @@ Layouts (all row-major):
                                                           sequence, as the decode-long
                                                           page lays K and V out
   paged k,v pool  [num_blocks, block_size, h_kv, d]       the same rows cut into blocks
+  x-split k pool  [num_blocks, h_kv, d/8, block_size, 8]  the kernel-map page's key_cache
+  x-split v pool  [num_blocks, h_kv, d, block_size]       (layout "paged_xsplit")
   block_table     [num_seqs, max_blocks_per_seq] int32    padded with -1
   ctx_lens        [num_seqs] int32
 
@@ -67,7 +69,7 @@ class DecodeCase:
     """One batch of decode-attention inputs (storage bits + metadata)."""
     name: str
     dtype: str
-    layout: str                 # "contiguous" or "paged"
+    layout: str                 # "contiguous", "paged" or "paged_xsplit"
     q: np.ndarray               # uint16 [num_seqs, h_q, d]
     k: np.ndarray               # uint16, layout-dependent (see module doc)
     v: np.ndarray
@@ -164,6 +166,22 @@ def paged_case(name: str, seed: int, ctx_lens, h_q: int, h_kv: int, d: int,
                       ctx_lens=ctx, block_table=table, h_q=h_q, h_kv=h_kv, d=d,
                       scale=float(1.0 / math.sqrt(d) if scale is None else scale),
                       block_size=block_size)
+
+
+XSPLIT_X = 8   # elements per 16-byte vector of fp16/bf16
+
+
+def xsplit_case(case: DecodeCase) -> DecodeCase:
+    """The same logical cache as a paged case, in the x-split pool layout:
+    k[b, j, d // 8, o, d % 8] and v[b, j, d, o] hold element d of slot o of KV
+    head j in block b (a pure rearrangement; NaN poison moves with its slot)."""
+    assert case.layout == "paged"
+    nb, bs, h_kv, d = case.k.shape
+    assert d % XSPLIT_X == 0
+    k = np.ascontiguousarray(
+        case.k.reshape(nb, bs, h_kv, d // XSPLIT_X, XSPLIT_X).transpose(0, 2, 3, 1, 4))
+    v = np.ascontiguousarray(case.v.transpose(0, 2, 3, 1))
+    return dataclasses.replace(case, name=case.name + "_xsplit", layout="paged_xsplit", k=k, v=v)
 
 
 # ---------------------------------------------------------------------------
