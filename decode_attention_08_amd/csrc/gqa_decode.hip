@@ -53,6 +53,14 @@ typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;            // tokens per wave iteration (two 16-token MFMA row blocks)
 constexpr int kMaxHeadsPerGroup = 8; // waves (KV heads) per partition workgroup, at most
+
+// Waves per partition workgroup for head dimension D.  Up to d = 128 a wave
+// fits in 256 registers, two waves per SIMD; at d = 256 its two K/V tiles
+// alone take 256, so a workgroup has at most 4 waves (one per SIMD) and each
+// wave may use the SIMD's whole 512-entry register file (arch + acc).
+__host__ __device__ constexpr int max_heads_per_group(int d) {
+  return d > 128 ? 4 : kMaxHeadsPerGroup;
+}
 constexpr int kMaxGrid = 2048;       // persistent grid cap (two partial slots per workgroup)
 constexpr int kMinChunkTiles = 2;    // smallest balanced share: 2 tiles = 64 tokens
 constexpr int kMaxSeqsBalanced = 8192;
@@ -411,7 +419,15 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   //      scheduling barriers keep each prefetch ahead of the compute it
   //      overlaps.
   int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
-  if (n > 0) {
+  if constexpr (D > 128) {
+    // d = 256: one register tile (32 KB of K/V per wave).  A wave waits for
+    // each tile; the other waves of the CU keep 3 x 32 KB in flight meanwhile.
+    Tile A;
+    for (int tb = t0; n > 0; --n, tb += kTile) {
+      load(A, tb);
+      compute(A, tb);
+    }
+  } else if (n > 0) {
     Tile A, B;
     int tb = t0;
     load(A, tb);
@@ -469,7 +485,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
 // cut into ceil(L / part_size) partitions whose partials land at [s, i, p].
 
 template <class DT, int D, bool PAGED, bool XS>
-__global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_fixed_kernel(Params a) {
+__global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x % a.max_parts;
@@ -515,7 +531,7 @@ __device__ __forceinline__ int64_t range_prefix(const Params& a, const int32_t* 
 }
 
 template <class DT, int D, bool PAGED, bool XS>
-__global__ __launch_bounds__(kMaxHeadsPerGroup * 64) void partition_balanced_kernel(Params a) {
+__global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balanced_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles, then the prefix
   __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
   const int lane = threadIdx.x & 63;
@@ -799,10 +815,11 @@ gqa_status_t resolve_policy(const gqa_policy_t* in, gqa_policy_t* out) {
   return GQA_OK;
 }
 
-// KV heads per workgroup: the largest divisor of h_kv that is at most 8, so
-// that a workgroup's waves read whole groups of adjacent heads of a token.
-int heads_per_group(int h_kv) {
-  for (int h = std::min(h_kv, kMaxHeadsPerGroup); h > 1; --h)
+// KV heads per workgroup: the largest divisor of h_kv that is at most
+// max_heads_per_group(d), so that a workgroup's waves read whole groups of
+// adjacent heads of a token.
+int heads_per_group(int h_kv, int d) {
+  for (int h = std::min(h_kv, max_heads_per_group(d)); h > 1; --h)
     if (h_kv % h == 0) return h;
   return 1;
 }
@@ -824,7 +841,7 @@ int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
 
 Plan make_plan(int num_seqs, int h_q, int h_kv, int d, int max_ctx, const gqa_policy_t& pol) {
   Plan pl{};
-  pl.hpw = heads_per_group(h_kv);
+  pl.hpw = heads_per_group(h_kv, d);
   pl.n_groups = h_kv / pl.hpw;
   pl.can_split = max_ctx > pol.v1_max_ctx;
   // the balanced scheduler keeps its per-sequence prefix in LDS as int32
@@ -966,8 +983,9 @@ gqa_status_t launch_layout(const Problem& pb, const Params& prm, const Plan& pl,
 template <class DT>
 gqa_status_t launch_dtype(const Problem& pb, const Params& prm, const Plan& pl, int ph,
                           hipStream_t st) {
-  return pb.d == 64 ? launch_layout<DT, 64>(pb, prm, pl, ph, st)
-                    : launch_layout<DT, 128>(pb, prm, pl, ph, st);
+  if (pb.d == 64) return launch_layout<DT, 64>(pb, prm, pl, ph, st);
+  if (pb.d == 128) return launch_layout<DT, 128>(pb, prm, pl, ph, st);
+  return launch_layout<DT, 256>(pb, prm, pl, ph, st);
 }
 
 gqa_status_t run(const Problem& pb) {
@@ -976,7 +994,7 @@ gqa_status_t run(const Problem& pb) {
     return GQA_ERR_BAD_SHAPE;
   if (pb.paged ? (pb.max_blocks <= 0) : (pb.s_kv < 0)) return GQA_ERR_BAD_SHAPE;
   if (pb.dtype != GQA_F16 && pb.dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
-  if (pb.d != 64 && pb.d != 128) return GQA_ERR_UNSUPPORTED;
+  if (pb.d != 64 && pb.d != 128 && pb.d != 256) return GQA_ERR_UNSUPPORTED;
   const int G = pb.h_q / pb.h_kv;
   if (G > 16) return GQA_ERR_UNSUPPORTED;
   int bs_shift = 0;

@@ -128,7 +128,7 @@ size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, in
                                  const gqa_policy_t* policy);
 
 /*
- * Paged decode.  d_head in {64, 128}; 1 <= G = h_q / h_kv <= 16 and h_q a
+ * Paged decode.  d_head in {64, 128, 256}; 1 <= G = h_q / h_kv <= 16 and h_q a
  * multiple of h_kv; block_size a power of two in [16, 256]; T_q = 1.
  * scale multiplies the logits (the workloads use 1 / sqrt(d_head)).  stream
  * is a hipStream_t (NULL: the default stream).  workspace may be NULL when

@@ -68,6 +68,9 @@ def test_workspace_size(gq):
     n = gq.workspace_size(3, 48, 12, 64, 4096, B)             # 12 KV heads: two groups of 6
     rows = 2 * 2048 * 6 * 4
     assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 64 * 4
+    n = gq.workspace_size(2, 16, 8, 256, 4096, B)             # d = 256: two groups of 4
+    rows = 2 * 2048 * 4 * 2
+    assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 256 * 4
     bad = gq.Policy(100, 0, 0, 0)
     assert gq.workspace_size(4, 32, 8, 128, 9000, bad) == 0
     assert gq.workspace_size(-1, 32, 8, 128, 9000, P) == 0
@@ -101,7 +104,8 @@ ERR = dict(NULL=1, SHAPE=2, UNSUP=3, ALIGN=4, WS=5, POLICY=6, SCALE=7)
     (dict(max_blocks=0), "SHAPE"),
     (dict(max_blocks=1 << 27, bs=16), "SHAPE"),
     (dict(d=96), "UNSUP"),
-    (dict(d=256), "UNSUP"),
+    (dict(d=512), "UNSUP"),
+    (dict(d=32), "UNSUP"),
     (dict(h_q=64, h_kv=2), "UNSUP"),
     (dict(bs=8), "UNSUP"),
     (dict(bs=48), "UNSUP"),

@@ -41,7 +41,7 @@ EDGE_LENGTHS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 511, 512, 513, 1000,
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_edge_lengths_all_policies(gq, dtype, d):
     case = W.paged_case(f"edges_{dtype}_{d}", 100 + d, EDGE_LENGTHS, h_q=16, h_kv=2, d=d,
                         dtype=dtype, extra_blocks=3)
@@ -213,9 +213,11 @@ def test_named_workloads_sampled(gq, name):
         assert_close(got, ref, case.dtype, what=f"{name} {pname}")
 
 
-@pytest.mark.parametrize("h_kv,G,d", [(12, 2, 64), (16, 1, 128), (6, 3, 128), (2, 16, 64)])
+@pytest.mark.parametrize("h_kv,G,d", [(12, 2, 64), (16, 1, 128), (6, 3, 128), (2, 16, 64),
+                                      (4, 3, 256), (8, 2, 256), (6, 1, 256), (2, 16, 256)])
 def test_head_groups(gq, h_kv, G, d):
-    """KV heads per workgroup = largest divisor of h_kv up to 8 (12 -> 6, 16 -> 8, 6 -> 6)."""
+    """KV heads per workgroup = largest divisor of h_kv up to 8, up to 4 at d = 256
+    (12 -> 6, 16 -> 8, 6 -> 6; at d = 256: 4 -> 4, 8 -> 4, 6 -> 3, 2 -> 2)."""
     case = W.paged_case(f"hg{h_kv}", 1200 + h_kv, [1300, 5, 333], h_q=G * h_kv, h_kv=h_kv, d=d,
                         dtype=W.BF16, extra_blocks=1)
     ref = R.decode(case)

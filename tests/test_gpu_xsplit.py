@@ -39,7 +39,7 @@ EDGE_LENGTHS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 511, 512, 513, 1000,
 
 
 @pytest.mark.parametrize("dtype", [W.F16, W.BF16])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_xsplit_edge_lengths(gq, dtype, d):
     rows = W.paged_case(f"xe_{dtype}_{d}", 2000 + d, EDGE_LENGTHS, h_q=16, h_kv=2, d=d,
                         dtype=dtype, extra_blocks=3)

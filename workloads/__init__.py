@@ -196,6 +196,8 @@ WORKLOADS = {
     "paged_b64": (2, "B=64, h_q=32, h_kv=8, d=128, bs=16, L~U{512..8192}, fp16, paged"),
     "long_128k": (3, "B=1, h_q=64, h_kv=8, d=128, S_kv=131072, bf16, contiguous"),
     "mixed_b256": (4, "B=256, h_q=32, h_kv=4, d=128, bs=16, L=clip(lognormal(ln 2048, 1), 64, 32768), fp16, paged"),
+    # head dimension 256 (a shape of its own, beside the five above)
+    "contig_d256": (5, "B=2, h_q=32, h_kv=8, d=256, S_kv=32768, bf16, contiguous"),
 }
 
 
@@ -212,7 +214,7 @@ def lognormal_lengths(seed: int, n: int, median: float, sigma: float,
 
 
 def workload(name: str, poison: bool = True) -> DecodeCase:
-    """Build one of the five named workloads (seed = 1000 + index)."""
+    """Build one of the named workloads (seed = 1000 + index)."""
     idx = WORKLOADS[name][0]
     seed = 1000 + idx
     if name == "tiny_contig":
@@ -227,4 +229,6 @@ def workload(name: str, poison: bool = True) -> DecodeCase:
     if name == "mixed_b256":
         ctx = lognormal_lengths(seed, 256, 2048.0, 1.0, 64, 32768)
         return paged_case(name, seed, ctx, 32, 4, 128, F16, 16, poison=poison)
+    if name == "contig_d256":
+        return contiguous_case(name, seed, 2, 32, 8, 256, 32768, BF16)
     raise KeyError(name)
