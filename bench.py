@@ -67,7 +67,7 @@ def _spin_cycles(torch, stream, seconds: float) -> int:
 
 XSPLIT_SUFFIX = "_xsplit"
 BENCH_WORKLOADS = ["tiny_contig", "contig_b8", "paged_b64", "long_128k", "mixed_b256",
-                   "contig_d256", "paged_b64_xsplit", "mixed_b256_xsplit"]
+                   "contig_d256", "paged_b64_t4", "paged_b64_xsplit", "mixed_b256_xsplit"]
 
 
 def bench_case(name: str):

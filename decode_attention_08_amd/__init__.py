@@ -7,6 +7,10 @@ built, importing this package raises.
 """
 from ._binding import (  # noqa: F401
     GQA_BF16,
+    GQA_KV_CONTIGUOUS,
+    GQA_KV_PAGED,
+    GQA_KV_PAGED_XSPLIT,
+    DecodeArgs,
     GQA_F16,
     GqaError,
     Policy,

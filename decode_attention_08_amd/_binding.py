@@ -19,9 +19,13 @@ lib = ctypes.CDLL(library_path)
 GQA_F16 = 0
 GQA_BF16 = 1
 
+GQA_KV_CONTIGUOUS = 0
+GQA_KV_PAGED = 1
+GQA_KV_PAGED_XSPLIT = 2
+
 EXPORTED_SYMBOLS = ("gqa_policy_default", "gqa_policy_pages", "gqa_decode_workspace_size",
                     "gqa_decode", "gqa_decode_xsplit", "gqa_decode_contiguous",
-                    "gqa_status_string")
+                    "gqa_decode_ex", "gqa_decode_ex_workspace_size", "gqa_status_string")
 X = 8   # elements per 16-byte vector of the x-split K layout
 
 
@@ -33,6 +37,20 @@ class Policy(ctypes.Structure):
     def __repr__(self):
         return (f"Policy(partition_size={self.partition_size}, v1_max_ctx={self.v1_max_ctx}, "
                 f"phases={self.phases})")
+
+
+class DecodeArgs(ctypes.Structure):
+    """gqa_decode_args_t (field order and types as in the header)."""
+    _fields_ = [("layout", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("ctx_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32),
+                ("t_q", ctypes.c_int32), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("s_kv", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("policy", ctypes.POINTER(Policy)),
+                ("stream", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -51,6 +69,10 @@ lib.gqa_decode_xsplit.restype = _I
 lib.gqa_decode_contiguous.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                       _P, ctypes.c_size_t, ctypes.POINTER(Policy), _P]
 lib.gqa_decode_contiguous.restype = _I
+lib.gqa_decode_ex.argtypes = [ctypes.POINTER(DecodeArgs)]
+lib.gqa_decode_ex.restype = _I
+lib.gqa_decode_ex_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
+lib.gqa_decode_ex_workspace_size.restype = ctypes.c_size_t
 lib.gqa_status_string.argtypes = [_I]
 lib.gqa_status_string.restype = ctypes.c_char_p
 
@@ -107,12 +129,15 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def _common(q, tensors, out):
+def _check_tensors(q, tensors):
     for name, t in tensors.items():
         _require(t.is_cuda, f"{name} must be a GPU tensor")
         _require(t.is_contiguous(), f"{name} must be contiguous")
         _require(t.device == q.device, f"{name} is on {t.device}, q on {q.device}")
-    _require(q.dim() == 3, "q must be [num_seqs, h_q, d_head]")
+    _require(q.dim() in (3, 4), "q must be [num_seqs, h_q, d_head] or [num_seqs, t_q, h_q, d_head]")
+
+
+def _out(q, out):
     if out is None:
         out = torch.empty_like(q)
     _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
@@ -135,46 +160,126 @@ def _stream(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _shapes(q, k, v, block_table, ctx_lens, layout: int):
+    """(B, t_q, h_q, d, h_kv, s_kv, max_blocks, block_size) of a call, checked."""
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    if q.dim() == 3:
+        B, h_q, d = q.shape
+        t_q = 1
+    else:
+        B, t_q, h_q, d = q.shape
+    s_kv = max_blocks = 0
+    bs = 16
+    if layout == GQA_KV_CONTIGUOUS:
+        _require(k.dim() == 4 and k.shape == v.shape, "k/v must be [B, S, h_kv, d]")
+        Bk, s_kv, h_kv, dk = k.shape
+        _require(Bk == B and dk == d, "k/v shape does not match q")
+    else:
+        _require(block_table.dtype == torch.int32 and block_table.dim() == 2,
+                 "block_table: int32 [B, max_blocks]")
+        _require(ctx_lens.dtype == torch.int32 and ctx_lens.dim() == 1, "ctx_lens: int32 [B]")
+        _require(block_table.shape[0] == B and ctx_lens.shape[0] == B, "batch sizes differ")
+        max_blocks = block_table.shape[1]
+        if layout == GQA_KV_PAGED_XSPLIT:
+            _require(k.dim() == 5 and v.dim() == 4,
+                     "x-split k must be [num_blocks, h_kv, d/8, bs, 8] and v [num_blocks, h_kv, d, bs]")
+            nb, h_kv, dx, bs, x = k.shape
+            _require(x == X and dx * X == d, "x-split k: last dims must be (d/8, bs, 8)")
+            _require(tuple(v.shape) == (nb, h_kv, d, bs), "x-split v must be [num_blocks, h_kv, d, bs]")
+        else:
+            _require(k.dim() == 4 and k.shape == v.shape, "k/v must be [num_blocks, bs, h_kv, d]")
+            _, bs, h_kv, dk = k.shape
+            _require(dk == d, "head dims differ")
+    return B, t_q, h_q, d, h_kv, s_kv, max_blocks, bs
+
+
+class PreparedCall:
+    """A decode call with its arguments marshalled once, for tight loops.
+
+    ``call(k=None, v=None, phases=None)`` invokes the C entry point again with
+    the same buffers, optionally another K/V pair of identical shape and
+    dtype, and optionally a different ``phases`` value.  The caller keeps
+    every tensor alive.  A 3-D q ([num_seqs, h_q, d]) goes through gqa_decode,
+    gqa_decode_xsplit or gqa_decode_contiguous; a 4-D q ([num_seqs, t_q, h_q,
+    d]) through gqa_decode_ex.
+    """
+
+    def __init__(self, layout: int, args: DecodeArgs, policy: Policy, keep):
+        self._policy = Policy(policy.partition_size, policy.v1_max_ctx, policy.phases, 0)
+        self._a = args
+        self._a.policy = ctypes.pointer(self._policy)
+        self._layout = layout
+        self._ex = args.t_q != 1 or keep[0].dim() == 4
+        self._keep = keep
+
+    def _invoke(self) -> int:
+        a = self._a
+        if self._ex:
+            return lib.gqa_decode_ex(ctypes.byref(a))
+        pol = ctypes.byref(self._policy)
+        if self._layout == GQA_KV_CONTIGUOUS:
+            return lib.gqa_decode_contiguous(a.q, a.k, a.v, a.out, a.num_seqs, a.s_kv, a.h_q,
+                                             a.h_kv, a.d_head, a.scale, a.dtype, a.workspace,
+                                             a.workspace_bytes, pol, a.stream)
+        fn = lib.gqa_decode_xsplit if self._layout == GQA_KV_PAGED_XSPLIT else lib.gqa_decode
+        return fn(a.q, a.k, a.v, a.block_table, a.ctx_lens, a.out, a.num_seqs,
+                  a.max_blocks_per_seq, a.h_q, a.h_kv, a.d_head, a.block_size, a.scale, a.dtype,
+                  a.workspace, a.workspace_bytes, pol, a.stream)
+
+    def __call__(self, k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                 phases: Optional[int] = None) -> None:
+        if k is not None:
+            self._a.k = k.data_ptr()
+            self._a.v = v.data_ptr()
+        if phases is not None:
+            self._policy.phases = phases
+        st = self._invoke()
+        if st != 0:
+            raise GqaError(st)
+
+
+def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
+            workspace=None, policy: Optional[Policy] = None, stream=None,
+            xsplit: bool = False) -> PreparedCall:
+    """Validate once and return a PreparedCall.  Paged when block_table is
+    given (the x-split pools with xsplit=True), contiguous otherwise.  q is
+    [num_seqs, h_q, d] or, for t_q query tokens per sequence, [num_seqs, t_q,
+    h_q, d]; out has q's shape."""
+    policy = policy_default() if policy is None else policy
+    if block_table is None:
+        _require(not xsplit, "the x-split layout is a paged layout (block_table required)")
+        layout = GQA_KV_CONTIGUOUS
+        _check_tensors(q, {"q": q, "k": k, "v": v})
+    else:
+        layout = GQA_KV_PAGED_XSPLIT if xsplit else GQA_KV_PAGED
+        _check_tensors(q, {"q": q, "k_cache": k, "v_cache": v, "block_table": block_table,
+                           "ctx_lens": ctx_lens})
+    out = _out(q, out)
+    B, t_q, h_q, d, h_kv, s_kv, max_blocks, bs = _shapes(q, k, v, block_table, ctx_lens, layout)
+    a = DecodeArgs(layout=layout, dtype=_dtype_code(q), q=_ptr(q), k=_ptr(k), v=_ptr(v),
+                   out=_ptr(out), block_table=_ptr(block_table), ctx_lens=_ptr(ctx_lens),
+                   num_seqs=B, t_q=t_q, h_q=h_q, h_kv=h_kv, d_head=d, s_kv=s_kv,
+                   max_blocks_per_seq=max_blocks, block_size=bs,
+                   scale=1.0 / math.sqrt(d) if scale is None else float(scale),
+                   stream=_stream(stream, q.device))
+    a.policy = ctypes.pointer(policy)
+    need = int(lib.gqa_decode_ex_workspace_size(ctypes.byref(a)))
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = ws_bytes
+    return PreparedCall(layout, a, policy, (q, k, v, block_table, ctx_lens, out, workspace))
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            block_table: torch.Tensor, ctx_lens: torch.Tensor, *, scale: Optional[float] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            policy: Optional[Policy] = None, stream=None) -> torch.Tensor:
-    """Paged GQA decode: q [B, h_q, d], k/v [num_blocks, bs, h_kv, d],
-    block_table [B, max_blocks] int32, ctx_lens [B] int32 -> out [B, h_q, d]."""
-    out = _common(q, {"q": q, "k_cache": k_cache, "v_cache": v_cache,
-                      "block_table": block_table, "ctx_lens": ctx_lens}, out)
-    _, bs, h_kv = _paged_shapes(q, k_cache, v_cache, block_table, ctx_lens, False)
-    B, h_q, d = q.shape
-    max_blocks = block_table.shape[1]
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
-    st = lib.gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_lens),
-                        _ptr(out), B, max_blocks, h_q, h_kv, d, bs, scale, _dtype_code(q),
-                        _ptr(workspace), ws_bytes, _pref(policy), _stream(stream, q.device))
-    if st != 0:
-        raise GqaError(st)
-    return out
-
-
-def _paged_shapes(q, k_cache, v_cache, block_table, ctx_lens, xsplit: bool):
-    """(num_blocks, block_size, h_kv) of a paged cache pair, checked."""
-    _require(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "q, k, v must share a dtype")
-    _require(block_table.dtype == torch.int32 and block_table.dim() == 2, "block_table: int32 [B, max_blocks]")
-    _require(ctx_lens.dtype == torch.int32 and ctx_lens.dim() == 1, "ctx_lens: int32 [B]")
-    B, h_q, d = q.shape
-    if xsplit:
-        _require(k_cache.dim() == 5 and v_cache.dim() == 4,
-                 "x-split k must be [num_blocks, h_kv, d/8, bs, 8] and v [num_blocks, h_kv, d, bs]")
-        nb, h_kv, dx, bs, x = k_cache.shape
-        _require(x == X and dx * X == d, "x-split k: last dims must be (d/8, bs, 8)")
-        _require(tuple(v_cache.shape) == (nb, h_kv, d, bs), "x-split v must be [num_blocks, h_kv, d, bs]")
-    else:
-        _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "k/v must be [num_blocks, bs, h_kv, d]")
-        nb, bs, h_kv, dk = k_cache.shape
-        _require(dk == d, "head dims differ")
-    _require(block_table.shape[0] == B and ctx_lens.shape[0] == B, "batch sizes differ")
-    return nb, bs, h_kv
+    """Paged GQA decode: q [B, h_q, d] (or [B, t_q, h_q, d]), k/v [num_blocks, bs, h_kv, d],
+    block_table [B, max_blocks] int32, ctx_lens [B] int32 -> out of q's shape."""
+    call = prepare(q, k_cache, v_cache, block_table=block_table, ctx_lens=ctx_lens, scale=scale,
+                   out=out, workspace=workspace, policy=policy, stream=stream)
+    call()
+    return call._keep[5]
 
 
 def decode_xsplit(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -184,105 +289,19 @@ def decode_xsplit(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   stream=None) -> torch.Tensor:
     """Paged GQA decode over the x-split layout: k [num_blocks, h_kv, d/8, bs, 8],
     v [num_blocks, h_kv, d, bs]; otherwise as decode()."""
-    out = _common(q, {"q": q, "k_cache": k_cache, "v_cache": v_cache,
-                      "block_table": block_table, "ctx_lens": ctx_lens}, out)
-    _, bs, h_kv = _paged_shapes(q, k_cache, v_cache, block_table, ctx_lens, True)
-    B, h_q, d = q.shape
-    max_blocks = block_table.shape[1]
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
-    st = lib.gqa_decode_xsplit(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                               _ptr(ctx_lens), _ptr(out), B, max_blocks, h_q, h_kv, d, bs, scale,
-                               _dtype_code(q), _ptr(workspace), ws_bytes, _pref(policy),
-                               _stream(stream, q.device))
-    if st != 0:
-        raise GqaError(st)
-    return out
+    call = prepare(q, k_cache, v_cache, block_table=block_table, ctx_lens=ctx_lens, scale=scale,
+                   out=out, workspace=workspace, policy=policy, stream=stream, xsplit=True)
+    call()
+    return call._keep[5]
 
 
 def decode_contiguous(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, policy: Optional[Policy] = None,
                       stream=None) -> torch.Tensor:
-    """Contiguous GQA decode: q [B, h_q, d], k/v [B, S, h_kv, d] -> out [B, h_q, d]."""
-    out = _common(q, {"q": q, "k": k, "v": v}, out)
-    _require(k.dim() == 4 and k.shape == v.shape, "k/v must be [B, S, h_kv, d]")
-    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
-    B, h_q, d = q.shape
-    Bk, S, h_kv, dk = k.shape
-    _require(Bk == B and dk == d, "k/v shape does not match q")
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = workspace_size(B, h_q, h_kv, d, S, policy)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
-    st = lib.gqa_decode_contiguous(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, h_q, h_kv, d,
-                                   scale, _dtype_code(q), _ptr(workspace), ws_bytes,
-                                   _pref(policy), _stream(stream, q.device))
-    if st != 0:
-        raise GqaError(st)
-    return out
-
-
-class PreparedCall:
-    """A decode call with its arguments marshalled once, for tight loops.
-
-    ``call(k=None, v=None, phases=None)`` invokes the C entry point again with
-    the same buffers, optionally another K/V pair of identical shape and
-    dtype, and optionally a different ``phases`` value.  The caller keeps
-    every tensor alive.
-    """
-
-    def __init__(self, fn, args, k_index, policy: Policy, keep):
-        self._fn = fn
-        self._args = list(args)
-        self._k_index = k_index
-        self._policy = Policy(policy.partition_size, policy.v1_max_ctx, policy.phases, 0)
-        self._pol_index = len(args) - 2
-        self._args[self._pol_index] = ctypes.byref(self._policy)
-        self._keep = keep
-
-    def __call__(self, k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
-                 phases: Optional[int] = None) -> None:
-        args = self._args
-        if k is not None:
-            args = list(args)
-            args[self._k_index] = k.data_ptr()
-            args[self._k_index + 1] = v.data_ptr()
-        if phases is not None:
-            self._policy.phases = phases
-        st = self._fn(*args)
-        if st != 0:
-            raise GqaError(st)
-
-
-def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
-            workspace=None, policy: Optional[Policy] = None, stream=None,
-            xsplit: bool = False) -> PreparedCall:
-    """Validate once (same checks as decode / decode_xsplit / decode_contiguous)
-    and return a PreparedCall.  Paged when block_table is given (x-split layout
-    with xsplit=True), contiguous otherwise."""
-    policy = policy_default() if policy is None else policy
-    if block_table is not None:
-        out = _common(q, {"q": q, "k_cache": k, "v_cache": v, "block_table": block_table,
-                          "ctx_lens": ctx_lens}, out)
-        _, bs, h_kv = _paged_shapes(q, k, v, block_table, ctx_lens, xsplit)
-        B, h_q, d = q.shape
-        max_blocks = block_table.shape[1]
-        need = workspace_size(B, h_q, h_kv, d, max_blocks * bs, policy)
-        workspace, ws_bytes = _workspace(workspace, need, q.device)
-        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(block_table), _ptr(ctx_lens), _ptr(out), B,
-                max_blocks, h_q, h_kv, d, bs, scale, _dtype_code(q), _ptr(workspace), ws_bytes,
-                None, _stream(stream, q.device))
-        fn = lib.gqa_decode_xsplit if xsplit else lib.gqa_decode
-        return PreparedCall(fn, args, 1, policy, (q, k, v, block_table, ctx_lens, out, workspace))
-    _require(not xsplit, "the x-split layout is a paged layout (block_table required)")
-    out = _common(q, {"q": q, "k": k, "v": v}, out)
-    B, h_q, d = q.shape
-    _, S, h_kv, _ = k.shape
-    need = workspace_size(B, h_q, h_kv, d, S, policy)
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, h_q, h_kv, d, scale, _dtype_code(q),
-            _ptr(workspace), ws_bytes, None, _stream(stream, q.device))
-    return PreparedCall(lib.gqa_decode_contiguous, args, 1, policy, (q, k, v, out, workspace))
+    """Contiguous GQA decode: q [B, h_q, d] (or [B, t_q, h_q, d]), k/v [B, S, h_kv, d]
+    -> out of q's shape."""
+    call = prepare(q, k, v, scale=scale, out=out, workspace=workspace, policy=policy,
+                   stream=stream)
+    call()
+    return call._keep[5]

@@ -111,6 +111,8 @@ struct Params {
   int h_q;
   int h_kv;
   int group;                    // G = h_q / h_kv
+  int tq;                       // query tokens per sequence (T_q)
+  int ncol;                     // G * T_q: query rows that share one KV head (<= 16)
   int hpw;                      // KV heads (waves) per workgroup
   int n_groups;                 // h_kv / hpw
   int s_kv;                     // contiguous length
@@ -178,9 +180,11 @@ struct Geo {
 // ------------------------------------------------- one wave, one segment --
 //
 // One wave computes the partial triple of tokens [t0, t1) of (sequence s,
-// KV head j) for the G query heads of that KV head and either stores the
+// KV head j) for the G * T_q query rows of that KV head (T_q query tokens of
+// G heads each, every one attending to all L_s keys) and either stores the
 // normalised output (complete == true: the segment is the whole sequence) or
-// the fp32 partial at pml[g * ml_stride], po[g * o_stride] for head g.  The
+// the fp32 partial at pml[c * ml_stride], po[c * o_stride] for column
+// c = tau * G + g.  The
 // wave walks its 32-token tiles in order and keeps the next tile's K and V
 // loads in flight while it computes the current one.  vt is the wave's LDS
 // tile (unused with XS).
@@ -208,13 +212,15 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   const int col = lane & 15;                     // head column / K row within a half
   const int grp = lane >> 4;                     // 16-lane group
   const int G = a.group;
-  const int head0 = j * G;
+  // column col < ncol is query token tau = col / G, query head j G + col % G
+  const bool live = col < a.ncol;
+  const int64_t qo_row = ((int64_t)s * a.tq + (live ? col / G : 0)) * a.h_q + j * G +
+                         (live ? col % G : 0);
 
   // ---- Q^T operand: lane holds q[head col][8 d of chunk kk*4+grp]; zero rows pad G to 16
   uint4_t qop[KK];
   {
-    const bool live = col < G;
-    const uint16_t* qrow = a.q + ((int64_t)s * a.h_q + head0 + (live ? col : 0)) * D;
+    const uint16_t* qrow = a.q + qo_row * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qop[kk] = live ? *reinterpret_cast<const uint4_t*>(qrow + 8 * (kk * 4 + grp))
@@ -454,9 +460,9 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   // ---- epilogue: each lane owns head col, d = 16 nb + 4 grp + r
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (col >= G) return;
+  if (!live) return;
   if (complete) {
-    uint16_t* dst = a.out + ((int64_t)s * a.h_q + head0 + col) * D + 4 * grp;
+    uint16_t* dst = a.out + qo_row * D + 4 * grp;
     const bool empty = t1 <= t0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -499,7 +505,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
   const int t0 = split ? p * a.part_size : 0;
   const int t1 = split ? min(t0 + a.part_size, L) : L;
   const int j = hg * a.hpw + w;
-  const int64_t row0 = (int64_t)s * a.h_q + j * a.group;
+  const int64_t row0 = ((int64_t)s * a.h_kv + j) * a.ncol;   // partial rows per (s, j, column)
   wave_segment<DT, D, PAGED, XS>(a, smem + (XS ? 0 : w * Geo<D>::V_TILE), s, j, t0, t1, !split,
                              a.part_ml + row0 * a.max_parts + p, a.max_parts,
                              a.part_o + (row0 * a.max_parts + p) * D, (int64_t)a.max_parts * D);
@@ -591,7 +597,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   int nt = seq_tiles(L);
   int hg = (int)((x0 - range_prefix<PAGED>(a, pref, s)) / nt);
   const int wg = blockIdx.x;
-  const int heads = a.hpw * a.group;             // query heads per head group
+  const int heads = a.hpw * a.ncol;              // partial rows per slot: (KV head, column)
 
   for (;;) {
     const int64_t rs = range_prefix<PAGED>(a, pref, s) + (int64_t)hg * nt;
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       } else {
         const int slot = 2 * wg + (rs <= x0 ? 0 : 1);
-        const int64_t hrow = (int64_t)slot * heads + w * a.group;
+        const int64_t hrow = (int64_t)slot * heads + w * a.ncol;
         wave_segment<DT, D, PAGED, XS>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
                                    a.part_o + hrow * D, D);
         if (sa == 0 && threadIdx.x == 0)
@@ -662,26 +668,32 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
   const int slot = threadIdx.x / kMergeLanes;
   const int r = threadIdx.x % kMergeLanes;
   const int sub = slot % SPI;                     // subset of the partials
-  const int item = blockIdx.x * HPB + slot / SPI; // (sequence, query head)
-  const int heads = a.hpw * a.group;
+  // one output row: (sequence s, query token tau, query head i) = item, the
+  // row-major index of out[num_seqs, T_q, h_q]
+  const int item = blockIdx.x * HPB + slot / SPI;
+  const int heads = a.hpw * a.ncol;               // partial rows per balanced slot
   // ---- the partial rows of this head; n = 0 for a head written in one pass.
   // No early return: with SPI > 1 every slot reaches the barrier below.
-  int n = 0, s = 0, i = 0;
+  int n = 0, s = 0, local = 0;
   int64_t base = 0;
   int4 d{0, 0, 0, 0};
-  if (item < a.num_seqs * a.h_q) {
-    s = item / a.h_q;
-    i = item % a.h_q;
+  const int rows_per_seq = a.tq * a.h_q;
+  if (item < a.num_seqs * rows_per_seq) {
+    s = item / rows_per_seq;
+    const int tau = (item % rows_per_seq) / a.h_q;
+    const int i = item % a.h_q;
+    const int j = i / a.group;                    // KV head
+    const int c = tau * a.group + i % a.group;    // column of KV head j's partial rows
     if constexpr (BALANCED) {
-      d = a.desc[s * a.n_groups + i / heads];
+      d = a.desc[s * a.n_groups + j / a.hpw];
       n = d.y == d.x ? 0 : d.y - d.x + 1;
+      local = (j % a.hpw) * a.ncol + c;
     } else {
       const int L = seq_len<PAGED>(a, s);
       n = L <= a.v1_max_ctx ? 0 : (L + a.part_size - 1) / a.part_size;
-      base = ((int64_t)s * a.h_q + i) * a.max_parts;
+      base = (((int64_t)s * a.h_kv + j) * a.ncol + c) * a.max_parts;
     }
   }
-  const int local = i % heads;
   auto row = [&](int k) -> int64_t {
     if constexpr (BALANCED)
       return (int64_t)(k == 0 ? d.z : 2 * (d.x + k)) * heads + local;
@@ -721,7 +733,7 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
       }
     }
   }
-  uint16_t* dst = a.out + ((int64_t)s * a.h_q + i) * D;
+  uint16_t* dst = a.out + (int64_t)item * D;
   if constexpr (SPI == 1) {
     if (n > 0) {
       uint32_t packed[E / 2];
@@ -777,6 +789,7 @@ constexpr int32_t kFallbackPartition = 512;
 struct Problem {
   bool paged;
   bool xsplit;        // paged caches in the x-split layout
+  int tq;             // query tokens per sequence
   const void* q;
   const void* k;
   const void* v;
@@ -839,7 +852,8 @@ int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
   return (int64_t)num_seqs * n_groups * std::max<int64_t>(1, ((int64_t)max_ctx + kTile - 1) / kTile);
 }
 
-Plan make_plan(int num_seqs, int h_q, int h_kv, int d, int max_ctx, const gqa_policy_t& pol) {
+Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
+               const gqa_policy_t& pol) {
   Plan pl{};
   pl.hpw = heads_per_group(h_kv, d);
   pl.n_groups = h_kv / pl.hpw;
@@ -851,12 +865,12 @@ Plan make_plan(int num_seqs, int h_q, int h_kv, int d, int max_ctx, const gqa_po
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
   if (!pl.can_split) return pl;
   if (pl.balanced) {
-    const size_t rows = (size_t)2 * kMaxGrid * pl.hpw * (h_q / h_kv);
+    const size_t rows = (size_t)2 * kMaxGrid * pl.hpw * (h_q / h_kv) * t_q;
     pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
     pl.ws_ml = align256(rows * sizeof(float2));
     pl.ws_o = rows * (size_t)d * sizeof(float);
   } else {
-    const size_t rows = (size_t)num_seqs * h_q * pl.max_parts;
+    const size_t rows = (size_t)num_seqs * h_q * t_q * pl.max_parts;
     pl.ws_desc = 0;
     pl.ws_ml = align256(rows * sizeof(float2));
     pl.ws_o = rows * (size_t)d * sizeof(float);
@@ -953,7 +967,7 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       const int64_t ranges = std::max<int64_t>(1, (int64_t)prm.num_seqs * pl.n_groups);
       per_head = (grid + ranges - 1) / ranges + 1;
     }
-    const int64_t items = (int64_t)prm.num_seqs * prm.h_q;
+    const int64_t items = (int64_t)prm.num_seqs * prm.tq * prm.h_q;
     // Slots per head: enough that a slot folds at most two batches of partials
     // and that the launch has 4096 slots or more (1024 waves), at most 16
     // unless a head has more than 512 partials.
@@ -996,7 +1010,8 @@ gqa_status_t run(const Problem& pb) {
   if (pb.dtype != GQA_F16 && pb.dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
   if (pb.d != 64 && pb.d != 128 && pb.d != 256) return GQA_ERR_UNSUPPORTED;
   const int G = pb.h_q / pb.h_kv;
-  if (G > 16) return GQA_ERR_UNSUPPORTED;
+  if (pb.tq < 1) return GQA_ERR_BAD_SHAPE;
+  if (G * pb.tq > 16) return GQA_ERR_UNSUPPORTED;
   int bs_shift = 0;
   if (pb.paged) {
     if (pb.block_size < 16 || pb.block_size > 256 || (pb.block_size & (pb.block_size - 1)))
@@ -1010,10 +1025,10 @@ gqa_status_t run(const Problem& pb) {
   const int64_t max_ctx64 = pb.paged ? (int64_t)pb.max_blocks * pb.block_size : pb.s_kv;
   if (max_ctx64 > (1 << 30)) return GQA_ERR_BAD_SHAPE;
   const int max_ctx = (int)max_ctx64;
-  const Plan pl = make_plan(pb.num_seqs, pb.h_q, pb.h_kv, pb.d, max_ctx, pol);
+  const Plan pl = make_plan(pb.num_seqs, pb.tq, pb.h_q, pb.h_kv, pb.d, max_ctx, pol);
   if (!pl.balanced && (int64_t)pl.max_parts * pl.n_groups * pb.num_seqs > INT32_MAX)
     return GQA_ERR_BAD_SHAPE;
-  if ((int64_t)pb.h_q * pb.num_seqs > INT32_MAX) return GQA_ERR_BAD_SHAPE;
+  if ((int64_t)pb.h_q * pb.tq * pb.num_seqs > INT32_MAX) return GQA_ERR_BAD_SHAPE;
   if (pb.num_seqs == 0) return GQA_OK;
 
   // ---- pointers
@@ -1048,6 +1063,8 @@ gqa_status_t run(const Problem& pb) {
   prm.h_q = pb.h_q;
   prm.h_kv = pb.h_kv;
   prm.group = G;
+  prm.tq = pb.tq;
+  prm.ncol = G * pb.tq;
   prm.hpw = pl.hpw;
   prm.n_groups = pl.n_groups;
   prm.s_kv = pb.s_kv;
@@ -1072,6 +1089,7 @@ gqa_status_t run_paged(bool xsplit, const void* q, const void* k_cache, const vo
   Problem pb{};
   pb.paged = true;
   pb.xsplit = xsplit;
+  pb.tq = 1;
   pb.q = q;
   pb.k = k_cache;
   pb.v = v_cache;
@@ -1119,7 +1137,7 @@ size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, in
   if (resolve_policy(policy, &pol) != GQA_OK) return 0;
   if (num_seqs < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || d_head <= 0 || max_ctx < 0)
     return 0;
-  return make_plan(num_seqs, h_q, h_kv, d_head, max_ctx, pol).ws_total;
+  return make_plan(num_seqs, 1, h_q, h_kv, d_head, max_ctx, pol).ws_total;
 }
 
 gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -1151,6 +1169,7 @@ gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, 
                                    const gqa_policy_t* policy, void* stream) {
   Problem pb{};
   pb.paged = false;
+  pb.tq = 1;
   pb.q = q;
   pb.k = k;
   pb.v = v;
@@ -1168,6 +1187,56 @@ gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, 
   pb.policy = policy;
   pb.stream = stream;
   return run(pb);
+}
+
+gqa_status_t gqa_decode_ex(const gqa_decode_args_t* args) {
+  if (!args) return GQA_ERR_NULL_PTR;
+  const gqa_decode_args_t& x = *args;
+  if (x.layout != GQA_KV_CONTIGUOUS && x.layout != GQA_KV_PAGED && x.layout != GQA_KV_PAGED_XSPLIT)
+    return GQA_ERR_UNSUPPORTED;
+  Problem pb{};
+  pb.paged = x.layout != GQA_KV_CONTIGUOUS;
+  pb.xsplit = x.layout == GQA_KV_PAGED_XSPLIT;
+  pb.tq = x.t_q;
+  pb.q = x.q;
+  pb.k = x.k;
+  pb.v = x.v;
+  pb.out = x.out;
+  pb.block_table = x.block_table;
+  pb.ctx_lens = x.ctx_lens;
+  pb.num_seqs = x.num_seqs;
+  pb.max_blocks = x.max_blocks_per_seq;
+  pb.s_kv = x.s_kv;
+  pb.h_q = x.h_q;
+  pb.h_kv = x.h_kv;
+  pb.d = x.d_head;
+  pb.block_size = pb.paged ? x.block_size : 16;
+  pb.scale = x.scale;
+  pb.dtype = x.dtype;
+  pb.ws = x.workspace;
+  pb.ws_bytes = x.workspace_bytes;
+  pb.policy = x.policy;
+  pb.stream = x.stream;
+  return run(pb);
+}
+
+size_t gqa_decode_ex_workspace_size(const gqa_decode_args_t* args) {
+  if (!args) return 0;
+  const gqa_decode_args_t& x = *args;
+  gqa_policy_t pol;
+  if (resolve_policy(x.policy, &pol) != GQA_OK) return 0;
+  if (x.num_seqs < 0 || x.t_q < 1 || x.h_q <= 0 || x.h_kv <= 0 || x.h_q % x.h_kv != 0 ||
+      x.d_head <= 0)
+    return 0;
+  int64_t max_ctx;
+  if (x.layout == GQA_KV_CONTIGUOUS)
+    max_ctx = x.s_kv;
+  else if (x.layout == GQA_KV_PAGED || x.layout == GQA_KV_PAGED_XSPLIT)
+    max_ctx = (int64_t)x.max_blocks_per_seq * x.block_size;
+  else
+    return 0;
+  if (max_ctx < 0 || max_ctx > (1 << 30)) return 0;
+  return make_plan(x.num_seqs, x.t_q, x.h_q, x.h_kv, x.d_head, (int)max_ctx, pol).ws_total;
 }
 
 const char* gqa_status_string(gqa_status_t status) {

@@ -129,7 +129,7 @@ size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, in
 
 /*
  * Paged decode.  d_head in {64, 128, 256}; 1 <= G = h_q / h_kv <= 16 and h_q a
- * multiple of h_kv; block_size a power of two in [16, 256]; T_q = 1.
+ * multiple of h_kv; block_size a power of two in [16, 256]; T_q = 1 (gqa_decode_ex takes more).
  * scale multiplies the logits (the workloads use 1 / sqrt(d_head)).  stream
  * is a hipStream_t (NULL: the default stream).  workspace may be NULL when
  * gqa_decode_workspace_size() is 0.  num_seqs == 0 returns GQA_OK and
@@ -173,6 +173,64 @@ gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, 
                                    float scale, gqa_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes,
                                    const gqa_policy_t* policy, void* stream);
+
+/*
+ * Extended call: every layout and T_q >= 1 query tokens per sequence through
+ * one argument block.
+ *
+ * T_q > 1.  The decode-long page's kernel takes Q as (T_q, h_q * d_head) per
+ * sequence, loads it as G * T_q rows against the same keys and stores O as
+ * (T_q, h_q * d_head); no mask is applied.  Here accordingly each of the T_q
+ * query tokens of sequence s attends to all L_s keys of the cache:
+ *   q, out  [num_seqs, t_q, h_q, d_head]
+ *   out[s, tau, i] = sum_t softmax_t(scale * <q[s, tau, i], K_s[t]>) V_s[t]
+ * The G * T_q query rows that share a KV head go through the same matrix-core
+ * products, so G * t_q <= 16.  With t_q == 1 the call equals gqa_decode /
+ * gqa_decode_xsplit / gqa_decode_contiguous on the same arguments.
+ *
+ * layout selects the cache: GQA_KV_CONTIGUOUS (k, v [num_seqs, s_kv, h_kv,
+ * d_head]; s_kv used, block fields ignored), GQA_KV_PAGED (the gqa_decode
+ * pools) or GQA_KV_PAGED_XSPLIT (the gqa_decode_xsplit pools; both paged
+ * layouts use block_table, ctx_lens, max_blocks_per_seq and block_size).
+ * Every other field, rule and error is as for those entry points; an unknown
+ * layout returns GQA_ERR_UNSUPPORTED, t_q < 1 GQA_ERR_BAD_SHAPE, and
+ * G * t_q > 16 GQA_ERR_UNSUPPORTED.
+ */
+typedef enum gqa_kv_layout {
+  GQA_KV_CONTIGUOUS = 0,
+  GQA_KV_PAGED = 1,
+  GQA_KV_PAGED_XSPLIT = 2
+} gqa_kv_layout_t;
+
+typedef struct gqa_decode_args {
+  gqa_kv_layout_t layout;
+  gqa_dtype_t dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* block_table;   /* paged layouts */
+  const int32_t* ctx_lens;      /* paged layouts */
+  int32_t num_seqs;
+  int32_t t_q;
+  int32_t h_q;
+  int32_t h_kv;
+  int32_t d_head;
+  int32_t s_kv;                 /* contiguous layout */
+  int32_t max_blocks_per_seq;   /* paged layouts */
+  int32_t block_size;           /* paged layouts */
+  float scale;
+  void* workspace;
+  size_t workspace_bytes;
+  const gqa_policy_t* policy;   /* NULL: gqa_policy_default() */
+  void* stream;                 /* hipStream_t; NULL: the default stream */
+} gqa_decode_args_t;
+
+gqa_status_t gqa_decode_ex(const gqa_decode_args_t* args);
+
+/* Workspace bytes gqa_decode_ex needs for *args (pointers are not read);
+ * 0 when nothing can be split or the sizes are invalid. */
+size_t gqa_decode_ex_workspace_size(const gqa_decode_args_t* args);
 
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status_t status);

@@ -134,12 +134,17 @@ def attend(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.
 
 
 def decode(case, heads: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
-    """Reference output [num_seqs, h_q, d] in float64 (or only the listed (s, i)).
+    """Reference output in float64: [num_seqs, h_q, d], or [num_seqs, T_q, h_q, d]
+    for a case with T_q query tokens per sequence (a 4-D q).  Only the listed
+    (s, i) rows are computed (for every query token); the others stay NaN.
 
-    Rows not listed in ``heads`` are left NaN.
+    T_q > 1 (decode-long page, tensor-layout docstring: Q is (T_q, h_q * d_head)
+    per sequence and O has the same shape; the page applies no mask): every
+    query token of sequence s attends to all L_s keys of the cache.
     """
     G = case.h_q // case.h_kv
-    out = np.full((case.num_seqs, case.h_q, case.d), np.nan, dtype=np.float64)
+    q = case.q if case.q.ndim == 4 else case.q[:, None]        # [B, T_q, h_q, d]
+    out = np.full((case.num_seqs, q.shape[1], case.h_q, case.d), np.nan, dtype=np.float64)
     if heads is None:
         heads = [(s, i) for s in range(case.num_seqs) for i in range(case.h_q)]
     by_pair = {}
@@ -147,9 +152,10 @@ def decode(case, heads: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarra
         by_pair.setdefault((s, kv_head(i, G)), []).append(i)
     for (s, j), idx in sorted(by_pair.items()):
         K, V = sequence_kv(case, s, j)
-        for i in idx:
-            out[s, i] = attend(upcast(case.q[s, i], case.dtype), K, V, case.scale)
-    return out
+        for tau in range(q.shape[1]):
+            for i in idx:
+                out[s, tau, i] = attend(upcast(q[s, tau, i], case.dtype), K, V, case.scale)
+    return out if case.q.ndim == 4 else out[:, 0]
 
 
 # ------------------------------------------------- partial triples, merge ---

@@ -156,3 +156,55 @@ def test_contiguous_validation(gq):
     pol = gq.policy_pages(v1_max_ctx=0)
     assert f(A, A, A, B, 2, 16, 8, 2, 64, 0.1, 1, None, 0, ctypes.byref(pol), None) == ERR["WS"]
     assert f(A, A, A, B, 2, 16, 8, 2, 64, math.nan, 1, None, 0, None, None) == ERR["SCALE"]
+
+
+def _ex(gq, **kw):
+    a = gq.DecodeArgs(layout=gq.GQA_KV_PAGED, dtype=0, q=A, k=A, v=A, out=B, block_table=A,
+                      ctx_lens=A, num_seqs=2, t_q=2, h_q=8, h_kv=2, d_head=128, s_kv=0,
+                      max_blocks_per_seq=4, block_size=16, scale=0.1, workspace=A,
+                      workspace_bytes=1 << 30, stream=None)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(t_q=0), "SHAPE"),
+    (dict(t_q=-3), "SHAPE"),
+    (dict(t_q=5), "UNSUP"),                 # G * t_q = 20 > 16
+    (dict(h_q=16, t_q=3), "UNSUP"),         # G = 8, G * t_q = 24
+    (dict(layout=3), "UNSUP"),
+    (dict(layout=0, s_kv=-1), "SHAPE"),
+    (dict(d_head=80), "UNSUP"),
+    (dict(q=None), "NULL"),
+    (dict(out=MIS), "ALIGN"),
+    (dict(scale=float("nan")), "SCALE"),
+    (dict(layout=2, block_size=8), "UNSUP"),
+])
+def test_ex_validation(gq, kw, code):
+    assert gq.lib.gqa_decode_ex(ctypes.byref(_ex(gq, **kw))) == ERR[code]
+
+
+def test_ex_null_and_empty(gq):
+    assert gq.lib.gqa_decode_ex(None) == ERR["NULL"]
+    assert gq.lib.gqa_decode_ex(ctypes.byref(_ex(gq, num_seqs=0, q=None, out=None))) == 0
+
+
+def test_ex_workspace_size(gq):
+    B = gq.policy_default()
+    P = gq.policy_pages(v1_max_ctx=0)
+    for t_q in (1, 2, 4):
+        # 512 blocks of 16: up to 8192 tokens, so sequences may split
+        a = _ex(gq, t_q=t_q, max_blocks_per_seq=512, policy=ctypes.pointer(B))
+        rows = 2 * 2048 * 2 * 4 * t_q                         # G = 4, 2 KV heads: one group
+        want = 256 + ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
+        assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(a)) == want
+        a = _ex(gq, t_q=t_q, max_blocks_per_seq=512, policy=ctypes.pointer(P))
+        rows = 2 * t_q * 8 * (8192 // 512)                    # fixed: [s, t_q, h_q, part]
+        want = ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
+        assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(a)) == want
+    a = _ex(gq, t_q=1, layout=0, s_kv=4096, policy=ctypes.pointer(B))
+    assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(a)) == \
+        gq.workspace_size(2, 8, 2, 128, 4096, B)
+    assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(_ex(gq, t_q=0))) == 0
+    assert gq.lib.gqa_decode_ex_workspace_size(None) == 0

@@ -12,6 +12,7 @@ gather against the contiguous layout.
 CPU) and checks that at least one pin fails for each, so the pins are known to
 bite.
 """
+import dataclasses
 import json
 import math
 import os
@@ -325,6 +326,29 @@ def pin_xsplit_equals_rows():
     assert np.array_equal(a, b)
 
 
+def pin_multi_token_rows():
+    """T_q query tokens per sequence: token tau gives exactly what a one-token
+    case with q[:, tau] gives, and the whole batch matches torch's
+    scaled_dot_product_attention with query length T_q and no mask."""
+    import torch
+    T, G, h_kv, d = 3, 2, 2, 8
+    case = W.paged_case("mt", 47, [5, 40, 17], h_q=G * h_kv, h_kv=h_kv, d=d, dtype=W.BF16,
+                        t_q=T, extra_blocks=1)
+    out = R.decode(case)
+    assert out.shape == (3, T, G * h_kv, d) and np.all(np.isfinite(out))
+    for tau in range(T):
+        one = dataclasses.replace(case, q=np.ascontiguousarray(case.q[:, tau]))
+        assert np.array_equal(out[:, tau], R.decode(one)), tau
+    for s, L in enumerate(case.ctx_lens):
+        K = np.stack([R.sequence_kv(case, s, j)[0] for j in range(h_kv)])   # [h_kv, L, d]
+        V = np.stack([R.sequence_kv(case, s, j)[1] for j in range(h_kv)])
+        q = torch.from_numpy(R.upcast(case.q[s], case.dtype)).permute(1, 0, 2)  # [h_q, T, d]
+        k = torch.from_numpy(K).repeat_interleave(G, dim=0)
+        v = torch.from_numpy(V).repeat_interleave(G, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=case.scale)
+        assert np.max(np.abs(out[s] - ref.permute(1, 0, 2).numpy())) <= 1e-13, s
+
+
 def pin_empty_sequence_zero():
     case = W.paged_case("e", 41, [0, 3], h_q=2, h_kv=1, d=4, dtype=W.F16, block_size=16)
     out = R.decode(case)
@@ -358,7 +382,7 @@ PINS = [pin_upcast_known_bits, pin_golden_closed_form, pin_brute_force_tiny, pin
         pin_weights_simplex, pin_two_token_closed_form, pin_invariances,
         pin_merge_split, pin_stability_and_argmax_limit, pin_sdpa_library_routine,
         pin_paged_equals_contiguous, pin_xsplit_gather_coded, pin_xsplit_equals_rows,
-        pin_empty_sequence_zero]
+        pin_multi_token_rows, pin_empty_sequence_zero]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -390,6 +414,13 @@ def _m_xsplit_chunks_transposed(k_pool, v_pool, block_table, s, j, L, block_size
         K[t, :] = k_pool[b, j, :, t % block_size, :].T.reshape(d)
         V[t, :] = v_pool[b, j, :, t % block_size]
     return K, V
+
+
+def _m_decode_first_token(case, heads=None):
+    if case.q.ndim == 4:
+        case = dataclasses.replace(case, q=np.ascontiguousarray(
+            np.repeat(case.q[:, :1], case.q.shape[1], axis=1)))
+    return _ORIG_DECODE(case, heads)
 
 
 def _m_kv_interleaved(i, group):
@@ -444,12 +475,14 @@ def _m_upcast_bf16_shift(bits, dtype):
 
 
 _ORIG_PARTIAL = R.partial
+_ORIG_DECODE = R.decode
 
 MUTANTS = {
     "logits_without_scale": ("logits", _m_no_scale),
     "paged_block_and_slot_swapped": ("gather_paged", _m_transposed_slot),
     "xsplit_chunks_transposed": ("gather_paged_xsplit", _m_xsplit_chunks_transposed),
     "kv_head_interleaved": ("kv_head", _m_kv_interleaved),
+    "every_query_token_reads_the_first": ("decode", _m_decode_first_token),
     "softmax_without_max_shift": ("softmax", _m_softmax_no_max),
     "softmax_unnormalised": ("softmax", _m_softmax_unnormalised),
     "merge_wrong_sign": ("merge", _m_merge_sign),

@@ -7,6 +7,7 @@ two K/V cache layouts.
 
 Layouts (all row-major):
   q               [num_seqs, h_q, d]                      fp16/bf16 bits (uint16)
+                  [num_seqs, t_q, h_q, d] with t_q > 1 query tokens per sequence
   contiguous k,v  [num_seqs, s_kv, h_kv, d]               one (S_kv, h_kv*d) slab per
                                                           sequence, as the decode-long
                                                           page lays K and V out
@@ -87,6 +88,10 @@ class DecodeCase:
         return int(self.q.shape[0])
 
     @property
+    def t_q(self) -> int:
+        return int(self.q.shape[1]) if self.q.ndim == 4 else 1
+
+    @property
     def group(self) -> int:
         return self.h_q // self.h_kv
 
@@ -105,12 +110,16 @@ def _streams(seed: int):
     return [np.random.default_rng(c) for c in ss.spawn(5)]
 
 
+def _q_shape(num_seqs: int, t_q: int, h_q: int, d: int):
+    return (num_seqs, h_q, d) if t_q == 1 else (num_seqs, t_q, h_q, d)
+
+
 def contiguous_case(name: str, seed: int, num_seqs: int, h_q: int, h_kv: int,
                     d: int, s_kv: int, dtype: str = F16,
-                    scale: Optional[float] = None) -> DecodeCase:
+                    scale: Optional[float] = None, t_q: int = 1) -> DecodeCase:
     """Contiguous cache: every sequence holds ``s_kv`` tokens."""
     _, _, rq, rk, rv = _streams(seed)
-    q = _normal_bits(rq, (num_seqs, h_q, d), dtype)
+    q = _normal_bits(rq, _q_shape(num_seqs, t_q, h_q, d), dtype)
     k = _normal_bits(rk, (num_seqs, s_kv, h_kv, d), dtype)
     v = _normal_bits(rv, (num_seqs, s_kv, h_kv, d), dtype)
     return DecodeCase(name=name, dtype=dtype, layout="contiguous", q=q, k=k, v=v,
@@ -123,7 +132,8 @@ def contiguous_case(name: str, seed: int, num_seqs: int, h_q: int, h_kv: int,
 def paged_case(name: str, seed: int, ctx_lens, h_q: int, h_kv: int, d: int,
                dtype: str = F16, block_size: int = 16,
                max_blocks: Optional[int] = None, extra_blocks: int = 0,
-               scale: Optional[float] = None, poison: bool = True) -> DecodeCase:
+               scale: Optional[float] = None, poison: bool = True,
+               t_q: int = 1) -> DecodeCase:
     """Paged cache with a seeded random permutation of physical blocks.
 
     The pool holds ``sum_s ceil(L_s/bs) + extra_blocks`` blocks; sequence s gets
@@ -146,7 +156,7 @@ def paged_case(name: str, seed: int, ctx_lens, h_q: int, h_kv: int, d: int,
     for s in range(num_seqs):
         table[s, :nblk[s]] = perm[off:off + nblk[s]]
         off += int(nblk[s])
-    q = _normal_bits(rq, (num_seqs, h_q, d), dtype)
+    q = _normal_bits(rq, _q_shape(num_seqs, t_q, h_q, d), dtype)
     pool_shape = (num_blocks, block_size, h_kv, d)
     k = _normal_bits(rk, pool_shape, dtype)
     v = _normal_bits(rv, pool_shape, dtype)
@@ -198,6 +208,8 @@ WORKLOADS = {
     "mixed_b256": (4, "B=256, h_q=32, h_kv=4, d=128, bs=16, L=clip(lognormal(ln 2048, 1), 64, 32768), fp16, paged"),
     # head dimension 256 (a shape of its own, beside the five above)
     "contig_d256": (5, "B=2, h_q=32, h_kv=8, d=256, S_kv=32768, bf16, contiguous"),
+    # four query tokens per sequence (T_q = 4, G * T_q = 16)
+    "paged_b64_t4": (6, "B=64, T_q=4, h_q=32, h_kv=8, d=128, bs=16, L~U{512..8192}, fp16, paged"),
 }
 
 
@@ -231,4 +243,7 @@ def workload(name: str, poison: bool = True) -> DecodeCase:
         return paged_case(name, seed, ctx, 32, 4, 128, F16, 16, poison=poison)
     if name == "contig_d256":
         return contiguous_case(name, seed, 2, 32, 8, 256, 32768, BF16)
+    if name == "paged_b64_t4":
+        ctx = uniform_lengths(seed, 64, 512, 8192)
+        return paged_case(name, seed, ctx, 32, 8, 128, F16, 16, poison=poison, t_q=4)
     raise KeyError(name)
