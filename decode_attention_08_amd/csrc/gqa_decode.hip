@@ -63,6 +63,7 @@ __host__ __device__ constexpr int max_heads_per_group(int d) {
 }
 constexpr int kMaxGrid = 2048;       // persistent grid cap (two partial slots per workgroup)
 constexpr int kMinChunkTiles = 2;    // smallest balanced share: 2 tiles = 64 tokens
+constexpr int kWavesPerCu = 4;       // balanced grid: waves per CU it aims for (see balanced_grid)
 constexpr int kMaxSeqsBalanced = 8192;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -879,9 +880,10 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
   return pl;
 }
 
-// Resident workgroups for a kernel, cached per (device, kernel, block, dynamic LDS).
-int resident_grid(const void* kernel, int block, size_t dyn_lds) {
-  struct Entry { int dev; const void* k; int block; size_t lds; int grid; };
+// Resident workgroups for a kernel, cached per (device, kernel, block, dynamic
+// LDS); *cus_out receives the device's CU count.
+int resident_grid(const void* kernel, int block, size_t dyn_lds, int* cus_out = nullptr) {
+  struct Entry { int dev; const void* k; int block; size_t lds; int grid; int cus; };
   static std::mutex mu;
   static Entry cache[64];
   static int n_cache = 0;
@@ -891,16 +893,19 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds) {
     std::lock_guard<std::mutex> lock(mu);
     for (int e = 0; e < n_cache; ++e)
       if (cache[e].dev == dev && cache[e].k == kernel && cache[e].block == block &&
-          cache[e].lds == dyn_lds)
+          cache[e].lds == dyn_lds) {
+        if (cus_out) *cus_out = cache[e].cus;
         return cache[e].grid;
+      }
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, dyn_lds) != hipSuccess)
     return 0;
   const int grid = std::max(1, cus * std::max(1, per_cu));
+  if (cus_out) *cus_out = cus;
   std::lock_guard<std::mutex> lock(mu);
-  if (n_cache < 64) cache[n_cache++] = Entry{dev, kernel, block, dyn_lds, grid};
+  if (n_cache < 64) cache[n_cache++] = Entry{dev, kernel, block, dyn_lds, grid, cus};
   return grid;
 }
 
@@ -910,13 +915,20 @@ size_t balanced_lds(const Params& prm, const Plan& pl) {
          (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
 }
 
-// Workgroups of the balanced partition launch: the resident count, at most
-// kMaxGrid, and no more than gives every workgroup kMinChunkTiles tiles.
+// Workgroups of the balanced partition launch: enough for kWavesPerCu waves
+// on every CU (one workgroup per CU when it has that many waves), at most the
+// resident count and kMaxGrid, and no more than gives every workgroup
+// kMinChunkTiles tiles.  More workgroups than that read no faster (4 waves of
+// two 16 KB tiles in flight already saturate a CU's share of HBM) but split
+// sequences into more partials for the merge.
 template <class DT, int D, bool PAGED, bool XS>
 int balanced_grid(const Params& prm, const Plan& pl) {
   const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS>);
-  const int resident = resident_grid(kern, 64 * pl.hpw, balanced_lds<D, PAGED, XS>(prm, pl));
-  if (resident <= 0) return 0;
+  int cus = 0;
+  const int resident0 = resident_grid(kern, 64 * pl.hpw, balanced_lds<D, PAGED, XS>(prm, pl), &cus);
+  if (resident0 <= 0) return 0;
+  const int per_cu = std::max(1, (kWavesPerCu + pl.hpw - 1) / pl.hpw);
+  const int resident = std::min(resident0, std::max(1, cus) * per_cu);
   const int64_t want =
       (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
   return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxGrid, resident, want}));
