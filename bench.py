@@ -9,9 +9,9 @@ step filled.
 
 Prints ONE JSON line.  `value` is K+V GB/s of the headline workload
 (algorithmic K+V bytes / wall time per step between synchronisations);
-`roofline` gives the partition kernel's own HBM roofline fraction, timed with
-HIP events on the launch stream around every partition launch of an eager
-pass over the same steps; `cpu_baseline` times
+`roofline` gives the partition kernel's own HBM roofline fraction, its mean
+launch duration timed with HIP events on the launch stream around the timed
+steps' partition launches issued back to back; `cpu_baseline` times
 the float64 oracle on a bounded sample of the same workload; `also` carries
 the other full-size workloads.
 
@@ -91,9 +91,10 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
 
     Pass 1 (headline): the `steps` steps captured once in a HIP graph and
     replayed between two synchronisations, so host launch overhead is not part
-    of the step time.  Pass 2 (kernel roofline): the same steps launched eagerly
-    with HIP events on the launch stream around the partition kernel and the
-    merge kernel of every step.
+    of the step time.  Pass 2 (kernel roofline): the steps' partition launches
+    back to back between one HIP event pair on the launch stream, then their
+    merge launches the same way (mean launch duration each).  Pass 3: eager
+    steps with an event pair around each, for the spread of step times.
     """
     import torch
     import decode_attention_08_amd as gq
@@ -142,28 +143,44 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
         gpu_step = ev_a.elapsed_time(ev_b) * 1e-3 / steps
         del graph
 
-        # ---- pass 2: eager steps with events around each kernel.  A bounded spin
-        # kernel first keeps the stream busy while the host enqueues every launch,
-        # so the events time back-to-back GPU work, not host launch latency.
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        # ---- pass 2 (kernel roofline): the `steps` partition launches of the
+        # timed steps back to back (each on its own K/V copy), one event pair
+        # around the batch; then the merge launches the same way.  A bounded
+        # spin kernel first keeps the stream busy while the host enqueues the
+        # batch, so the events time GPU work, not host launch latency.
         spin = _spin_cycles(torch, stream, seconds=max(2e-3, 400e-6 * steps))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         torch.cuda.synchronize()
+        torch.cuda._sleep(spin)
+        ev[0].record(stream)
+        for i in range(steps):
+            call(ks[(warmup + i) % copies], vs[(warmup + i) % copies], phases=1)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        mean_part = ev[0].elapsed_time(ev[1]) / steps              # ms
+        mean_merge = 0.0
+        if has_merge:
+            torch.cuda._sleep(spin)
+            ev[2].record(stream)
+            for i in range(steps):
+                call(phases=2)
+            ev[3].record(stream)
+            torch.cuda.synchronize()
+            mean_merge = ev[2].elapsed_time(ev[3]) / steps
+
+        # ---- pass 3 (step-time spread): eager steps with an event pair around
+        # each; includes each launch's dispatch, so it reads above pass 1.
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda._sleep(spin)
         t1 = time.perf_counter()
         for i in range(steps):
             kk, vv = ks[(warmup + i) % copies], vs[(warmup + i) % copies]
             evs[i][0].record(stream)
-            call(kk, vv, phases=1)
+            call(kk, vv, phases=3)
             evs[i][1].record(stream)
-            if has_merge:
-                call(kk, vv, phases=2)
-            evs[i][2].record(stream)
         torch.cuda.synchronize()
         eager_wall = (time.perf_counter() - t1) / steps
-    part = sorted(e[0].elapsed_time(e[1]) for e in evs)      # ms
-    merge = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    step_ev = sorted(e[0].elapsed_time(e[2]) for e in evs)
-    mean_part = sum(part) / len(part)
+    step_ev = sorted(e[0].elapsed_time(e[1]) for e in evs)
     res = {"workload": case.name, "policy": policy_name,
            "partition_size": pol.partition_size, "v1_max_ctx": pol.v1_max_ctx,
            "kv_bytes": case.kv_bytes, "copies": copies,
@@ -172,8 +189,7 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
            "gbs": case.kv_bytes / wall / 1e9,
            "eager_us_per_step": eager_wall * 1e6,
            "partition_us_mean": mean_part * 1e3,
-           "partition_us_median": part[len(part) // 2] * 1e3,
-           "merge_us_mean": sum(merge) / len(merge) * 1e3,
+           "merge_us_mean": mean_merge * 1e3,
            "step_us_events_median": step_ev[len(step_ev) // 2] * 1e3,
            "step_us_events_p10": step_ev[len(step_ev) // 10] * 1e3,
            "step_us_events_p90": step_ev[(9 * len(step_ev)) // 10] * 1e3,
@@ -323,8 +339,8 @@ def main():
                 json.dump(table, f, indent=1, sort_keys=True)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not built.", file=sys.stderr)
         return 2
 
     import torch
@@ -384,7 +400,9 @@ def main():
         "us_per_step": round(head["us_per_step"], 2),
         "pct_of_peak": round(head["pct_of_peak"], 2),
         "timing": "graph replay of the timed steps between synchronisations (wall clock); "
-                  "kernel times from an eager pass of the same steps with HIP events",
+                  "kernel times: HIP events around the steps' partition (then merge) "
+                  "launches issued back to back; step_us_events: events around each "
+                  "eager step, dispatch included",
         "eager_us_per_step": round(head["eager_us_per_step"], 2),
         "step_us_events": {"median": round(head["step_us_events_median"], 2),
                            "p10": round(head["step_us_events_p10"], 2),

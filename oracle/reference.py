@@ -15,7 +15,7 @@ t in [0, L_s):
 Every stored fp16/bf16 operand is upcast exactly to float64 first, so input
 quantisation is not part of any error measured against this module.
 
-Readings where the pages are silent or loose (each listed in the design doc):
+Readings where the pages are silent or loose:
   * ``scale`` multiplies the logits (the decode-long page's ``tl.dot`` carries
     no softmax scale; the workloads use 1/sqrt(d)).
   * K enters as a true transpose (the page's reshape-not-transpose load is a
