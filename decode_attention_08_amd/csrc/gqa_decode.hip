@@ -50,6 +50,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 32;            // tokens per wave iteration (two 16-token MFMA row blocks)
 constexpr int kMaxHeadsPerGroup = 8; // waves (KV heads) per partition workgroup, at most
@@ -146,6 +147,17 @@ __device__ __forceinline__ int seq_len(const Params& a, int s) {
   }
 }
 
+// K and V are read exactly once per call, so their loads are non-temporal:
+// they do not displace the partials, tables and queries the caches hold (on
+// MI355X this raises the partition kernel's read rate by about a tenth).
+template <class T, bool NT>
+__device__ __forceinline__ T load_stream(const uint16_t* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else
+    return *reinterpret_cast<const T*>(p);
+}
+
 // tiles of 32 tokens a sequence occupies in the balanced work space (an empty
 // sequence still occupies one, so that exactly one workgroup writes its zero row)
 __device__ __forceinline__ int seq_tiles(int L) { return max(1, (L + kTile - 1) / kTile); }
@@ -198,7 +210,7 @@ struct Geo {
 // P.V product needs, so V goes from HBM to the matrix core without the LDS
 // tile.
 
-template <class DT, int D, bool PAGED, bool XS = false>
+template <class DT, int D, bool PAGED, bool XS, bool NT>
 __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int s, int j, int t0,
                                              int t1, bool complete, float2* pml,
                                              int64_t ml_stride, float* po, int64_t o_stride) {
@@ -244,7 +256,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   };
   struct TileX {
     uint4_t k[2][KK];
-    uint2 v[NB][2];                               // [d block][half]: 4 tokens of d = 16 nb + col
+    uint2_t v[NB][2];                             // [d block][half]: 4 tokens of d = 16 nb + col
   };
   using Tile = std::conditional_t<XS, TileX, TileRows>;
 
@@ -280,7 +292,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const uint16_t* kbase = kb[hb] + ((int64_t)(kk * 4) << (a.bs_shift + 3));
-          T.k[hb][kk] = *reinterpret_cast<const uint4_t*>(kbase + k_lane);
+          T.k[hb][kk] = load_stream<uint4_t, NT>(kbase + k_lane);
         }
       }
 #pragma unroll
@@ -288,7 +300,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const uint16_t* vbase = vb[hb] + ((int64_t)(16 * nb) << a.bs_shift);
-          T.v[nb][hb] = *reinterpret_cast<const uint2*>(vbase + v_lane);
+          T.v[nb][hb] = load_stream<uint2_t, NT>(vbase + v_lane);
         }
     } else {
 #pragma unroll
@@ -310,14 +322,14 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
         const int r = it * RPI + lane / CH;
         const int hb = r >> 4;                      // uniform per instruction
         const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
-        T.v[it] = *reinterpret_cast<const uint4_t*>(vb[hb] + off);
+        T.v[it] = load_stream<uint4_t, NT>(vb[hb] + off);
       }
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          T.k[hb][kk] = *reinterpret_cast<const uint4_t*>(kb[hb] + roff + 8 * (kk * 4 + grp));
+          T.k[hb][kk] = load_stream<uint4_t, NT>(kb[hb] + roff + 8 * (kk * 4 + grp));
       }
     }
   };
@@ -379,7 +391,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
     if constexpr (XS) {
       // O^T += V^T . P^T with V^T straight from the loads; in a tile that
       // reaches past t1, V elements of tokens >= t1 (possibly NaN) are cleared
-      uint2 keep[2] = {make_uint2(~0u, ~0u), make_uint2(~0u, ~0u)};
+      uint2_t keep[2] = {uint2_t{~0u, ~0u}, uint2_t{~0u, ~0u}};
       if (tb + kTile > t1) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -490,8 +502,11 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
 // head of the group; the kernel-map page's decomposition: a sequence of at
 // most v1_max_ctx tokens is one partition written directly, a longer one is
 // cut into ceil(L / part_size) partitions whose partials land at [s, i, p].
+// NT selects non-temporal K/V loads.  They raise the read rate when many
+// workgroups stream at once, but a lone wave that walks a whole long sequence
+// is latency-bound and runs faster with ordinary loads (the host decides).
 
-template <class DT, int D, bool PAGED, bool XS>
+template <class DT, int D, bool PAGED, bool XS, bool NT>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -507,9 +522,10 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
   const int t1 = split ? min(t0 + a.part_size, L) : L;
   const int j = hg * a.hpw + w;
   const int64_t row0 = ((int64_t)s * a.h_kv + j) * a.ncol;   // partial rows per (s, j, column)
-  wave_segment<DT, D, PAGED, XS>(a, smem + (XS ? 0 : w * Geo<D>::V_TILE), s, j, t0, t1, !split,
-                             a.part_ml + row0 * a.max_parts + p, a.max_parts,
-                             a.part_o + (row0 * a.max_parts + p) * D, (int64_t)a.max_parts * D);
+  wave_segment<DT, D, PAGED, XS, NT>(
+      a, smem + (XS ? 0 : w * Geo<D>::V_TILE), s, j, t0, t1, !split,
+      a.part_ml + row0 * a.max_parts + p, a.max_parts, a.part_o + (row0 * a.max_parts + p) * D,
+      (int64_t)a.max_parts * D);
 }
 
 // ------------------------------------------------------- balanced kernel --
@@ -608,7 +624,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
     const int j = hg * a.hpw + w;
     if (L <= a.v1_max_ctx) {
       if (rs >= x0) {                            // owned: the whole range, never split
-        wave_segment<DT, D, PAGED, XS>(a, vt, s, j, 0, L, true, nullptr, 0, nullptr, 0);
+        wave_segment<DT, D, PAGED, XS, true>(a, vt, s, j, 0, L, true, nullptr, 0, nullptr, 0);
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       }
     } else {
@@ -617,12 +633,12 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
       const int t0 = (int)(sa * kTile);
       const int t1 = (int)min(sb * kTile, (int64_t)L);
       if (sa == 0 && sb == nt) {
-        wave_segment<DT, D, PAGED, XS>(a, vt, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
+        wave_segment<DT, D, PAGED, XS, true>(a, vt, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       } else {
         const int slot = 2 * wg + (rs <= x0 ? 0 : 1);
         const int64_t hrow = (int64_t)slot * heads + w * a.ncol;
-        wave_segment<DT, D, PAGED, XS>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
+        wave_segment<DT, D, PAGED, XS, true>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
                                    a.part_o + hrow * D, D);
         if (sa == 0 && threadIdx.x == 0)
           a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
@@ -964,8 +980,16 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
         return GQA_ERR_LAUNCH;
     } else {
       const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;
-      if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS>),
-                          dim3((unsigned)grid), dim3(block), args, tiles_lds, stream) != hipSuccess)
+      // Non-temporal loads unless some wave may walk more than one partition's
+      // worth of tokens in a single pass (a sequence of up to v1_max_ctx tokens
+      // that is not split); a contiguous cache longer than v1_max_ctx splits
+      // every sequence.
+      const bool short_walks = prm.v1_max_ctx <= prm.part_size || (!PAGED && prm.s_kv > prm.v1_max_ctx);
+      const void* kern =
+          short_walks ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true>)
+                      : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false>);
+      if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(block), args, tiles_lds, stream) !=
+          hipSuccess)
         return GQA_ERR_LAUNCH;
     }
   }
