@@ -115,7 +115,8 @@ struct Params {
   int group;                    // G = h_q / h_kv
   int tq;                       // query tokens per sequence (T_q)
   int ncol;                     // G * T_q: query rows that share one KV head (<= 16)
-  int hpw;                      // KV heads (waves) per workgroup
+  int hpw;                      // KV heads per workgroup
+  int wph;                      // waves per KV head (they split each segment's tiles)
   int n_groups;                 // h_kv / hpw
   int s_kv;                     // contiguous length
   int max_blocks;               // paged table width
@@ -210,9 +211,10 @@ struct Geo {
 // P.V product needs, so V goes from HBM to the matrix core without the LDS
 // tile.
 
-template <class DT, int D, bool PAGED, bool XS, bool NT>
-__device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int s, int j, int t0,
-                                             int t1, bool complete, float2* pml,
+template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
+__device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, uint16_t* vt,
+                                             float2* mlx, int s, int j, int t0, int t1,
+                                             bool complete, float2* pml,
                                              int64_t ml_stride, float* po, int64_t o_stride) {
   using Gm = Geo<D>;
   constexpr int KK = Gm::KK, NB = Gm::NB, CH = Gm::CH, RPI = Gm::RPI, NIT = Gm::NIT;
@@ -222,6 +224,22 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   t0 = __builtin_amdgcn_readfirstlane(t0);
   t1 = __builtin_amdgcn_readfirstlane(t1);
   const int lane = threadIdx.x & 63;
+  // SPLIT: the wph waves of a KV head split the segment's tiles evenly and
+  // sub-wave u walks [u0, u1); tile masking then uses u1, the output logic the
+  // whole segment.  (A compile-time switch: the extra scalars would push the
+  // one-wave-per-head kernels past their register budget.)
+  int sub = 0, w = 0;
+  bool seg_empty = false;
+  if constexpr (SPLIT) {
+    w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    sub = w / a.hpw;
+    const int n_all = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
+    const int u0 = t0 + kTile * (sub * n_all / a.wph);
+    const int u1 = min(t1, t0 + kTile * ((sub + 1) * n_all / a.wph));
+    seg_empty = t1 <= t0;
+    t0 = u0;
+    t1 = u1;
+  }
   const int col = lane & 15;                     // head column / K row within a half
   const int grp = lane >> 4;                     // 16-lane group
   const int G = a.group;
@@ -473,14 +491,42 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* vt, int 
   // ---- epilogue: each lane owns head col, d = 16 nb + 4 grp + r
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  if constexpr (SPLIT) {
+    // Merge the wph sub-wave states of this KV head ("_merge_running" in sub-wave
+    // order, an empty share (-inf, 0, 0) weighing 0) into sub-wave 0, through
+    // LDS: each wave parks its accumulators in its own tile region (64 D bytes,
+    // the size of a V tile) and its (m, l) per column in mlx.  Every wave of the
+    // workgroup walks the same segments, so the barriers are uniform.
+    float4_t* park = reinterpret_cast<float4_t*>(vt);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) park[nb * 64 + lane] = acc[nb];
+    if (grp == 0) mlx[w * 16 + col] = make_float2(m_run, l_run);
+    __syncthreads();
+    if (sub == 0) {
+      for (int u = 1; u < a.wph; ++u) {
+        const int w2 = w + u * a.hpw;
+        const float2 o2 = mlx[w2 * 16 + col];
+        const float m_new = fmaxf(m_run, o2.x);
+        const float a1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float a2 = o2.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o2.x - m_new);
+        const float4_t* other = reinterpret_cast<const float4_t*>(smem + w2 * Geo<D>::V_TILE);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = acc[nb] * a1 + other[nb * 64 + lane] * a2;
+        l_run = l_run * a1 + o2.y * a2;
+        m_run = m_new;
+      }
+    }
+    __syncthreads();                              // parked states read before the next segment
+    if (sub != 0) return;
+  }
   if (!live) return;
   if (complete) {
     uint16_t* dst = a.out + qo_row * D + 4 * grp;
-    const bool empty = t1 <= t0;
+    if constexpr (!SPLIT) seg_empty = t1 <= t0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint32_t w01, w23;
-      if (empty) {
+      if (seg_empty) {
         w01 = w23 = 0u;
       } else {
         w01 = DT::narrow(acc[nb][0] / l_run) | (DT::narrow(acc[nb][1] / l_run) << 16);
@@ -522,8 +568,8 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
   const int t1 = split ? min(t0 + a.part_size, L) : L;
   const int j = hg * a.hpw + w;
   const int64_t row0 = ((int64_t)s * a.h_kv + j) * a.ncol;   // partial rows per (s, j, column)
-  wave_segment<DT, D, PAGED, XS, NT>(
-      a, smem + (XS ? 0 : w * Geo<D>::V_TILE), s, j, t0, t1, !split,
+  wave_segment<DT, D, PAGED, XS, NT, false>(
+      a, smem, smem + (XS ? 0 : w * Geo<D>::V_TILE), nullptr, s, j, t0, t1, !split,
       a.part_ml + row0 * a.max_parts + p, a.max_parts, a.part_o + (row0 * a.max_parts + p) * D,
       (int64_t)a.max_parts * D);
 }
@@ -553,16 +599,19 @@ __device__ __forceinline__ int64_t range_prefix(const Params& a, const int32_t* 
     return (int64_t)s * a.n_groups * seq_tiles(a.s_kv);
 }
 
-template <class DT, int D, bool PAGED, bool XS>
+template <class DT, int D, bool PAGED, bool XS, bool SPLIT>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balanced_kernel(Params a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles, then the prefix
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // wave tiles, then the prefix
   __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
+  __shared__ float2 mlx[kMaxHeadsPerGroup * 16];                     // sub-wave (m, l) exchange
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;                // = hpw
-  constexpr int VT = XS ? 0 : Geo<D>::V_TILE;     // the x-split layout stages nothing
-  uint16_t* const vt = smem + w * VT;
-  int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * VT);
+  const int nw = blockDim.x >> 6;                // = hpw * wph
+  // per-wave tiles: V staging (row layout) and the sub-wave state exchange;
+  // the x-split layout with one wave per head needs neither
+  constexpr int tile_elems = (XS && !SPLIT) ? 0 : Geo<D>::V_TILE;
+  uint16_t* const vt = smem + w * tile_elems;
+  int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * tile_elems);
 
   // ---- paged: pref[s] = n_groups * (tiles of sequences < s); arithmetic when contiguous
   int64_t total;
@@ -621,10 +670,10 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
     if (rs >= x1) break;
     const int64_t re = rs + nt;
     const int r = s * a.n_groups + hg;
-    const int j = hg * a.hpw + w;
+    const int j = hg * a.hpw + (SPLIT ? w % a.hpw : w);
     if (L <= a.v1_max_ctx) {
       if (rs >= x0) {                            // owned: the whole range, never split
-        wave_segment<DT, D, PAGED, XS, true>(a, vt, s, j, 0, L, true, nullptr, 0, nullptr, 0);
+        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, 0, L, true, nullptr, 0, nullptr, 0);
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       }
     } else {
@@ -633,12 +682,12 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
       const int t0 = (int)(sa * kTile);
       const int t1 = (int)min(sb * kTile, (int64_t)L);
       if (sa == 0 && sb == nt) {
-        wave_segment<DT, D, PAGED, XS, true>(a, vt, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
+        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
         if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
       } else {
         const int slot = 2 * wg + (rs <= x0 ? 0 : 1);
-        const int64_t hrow = (int64_t)slot * heads + w * a.ncol;
-        wave_segment<DT, D, PAGED, XS, true>(a, vt, s, j, t0, t1, false, a.part_ml + hrow, 1,
+        const int64_t hrow = (int64_t)slot * heads + (SPLIT ? w % a.hpw : w) * a.ncol;
+        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, false, a.part_ml + hrow, 1,
                                    a.part_o + hrow * D, D);
         if (sa == 0 && threadIdx.x == 0)
           a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
@@ -678,7 +727,9 @@ __host__ __device__ constexpr int merge_heads_per_block(int spi) {
 
 template <class DT, int D, bool PAGED, bool BALANCED, int SPI>
 __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
-  constexpr int E = D / kMergeLanes;              // floats per lane: 8 (d = 128) or 4 (d = 64)
+  constexpr int E = D / kMergeLanes;              // floats per lane: d / 16
+  // a 1024-thread block leaves 128 registers per lane: fewer loads in flight at d = 256
+  constexpr int U = (merge_block(SPI) > 256 && D > 128) ? kMergeUnroll / 2 : kMergeUnroll;
   constexpr int SLOTS = merge_block(SPI) / kMergeLanes;
   constexpr int HPB = merge_heads_per_block(SPI);
   static_assert(E % 4 == 0 && HPB >= 1 && HPB * SPI == SLOTS, "merge shape");
@@ -722,11 +773,11 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int k0 = sub; k0 < n; k0 += kMergeUnroll * SPI) {
-    float2 t2[kMergeUnroll];
-    float4_t v[kMergeUnroll][E / 4];
+  for (int k0 = sub; k0 < n; k0 += U * SPI) {
+    float2 t2[U];
+    float4_t v[U][E / 4];
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (k0 + u * SPI < n) {
         const int64_t rw = row(k0 + u * SPI);
         t2[u] = a.part_ml[rw];
@@ -736,7 +787,7 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (k0 + u * SPI < n) {
         const float m_new = fmaxf(m, t2[u].x);    // finite: a partial holds at least one token
         const float a_old = __builtin_amdgcn_exp2f(m - m_new);
@@ -857,7 +908,8 @@ int heads_per_group(int h_kv, int d) {
 // How a call is decomposed once the sizes are known.
 struct Plan {
   bool balanced;
-  int hpw;            // KV heads (waves) per workgroup
+  int hpw;            // KV heads per workgroup
+  int wph;            // waves per KV head: hpw * wph waves per workgroup
   int n_groups;       // h_kv / hpw
   int part_size;      // fixed mode
   int max_parts;      // fixed mode
@@ -873,11 +925,19 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
                const gqa_policy_t& pol) {
   Plan pl{};
   pl.hpw = heads_per_group(h_kv, d);
+  // a workgroup of fewer than the full complement of waves gives each KV head
+  // several waves, which split its segments (more loads in flight per head)
+  pl.wph = 1;
   pl.n_groups = h_kv / pl.hpw;
   pl.can_split = max_ctx > pol.v1_max_ctx;
   // the balanced scheduler keeps its per-sequence prefix in LDS as int32
   pl.balanced = pol.partition_size == 0 && num_seqs <= kMaxSeqsBalanced &&
                 upper_tiles(num_seqs, pl.n_groups, max_ctx) < (int64_t)INT32_MAX / 2;
+  // Groups of one or two KV heads (small h_kv) get several waves per head,
+  // which split each segment's tiles: a lone wave per head walking a short
+  // sequence is latency-bound.  Larger groups have waves enough; on a batch of
+  // 256 sequences of ~3400 tokens with four KV heads the split cost 2%.
+  if (pl.balanced && pl.hpw <= 2) pl.wph = max_heads_per_group(d) / pl.hpw;
   pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
   if (!pl.can_split) return pl;
@@ -925,9 +985,22 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds, int* cus_out = 
   return grid;
 }
 
+// Per-wave LDS tiles: V staging (row layout) and the sub-wave state exchange.
+template <int D, bool XS>
+size_t tiles_lds(const Plan& pl) {
+  return (XS && pl.wph == 1) ? 0 : (size_t)pl.hpw * pl.wph * Geo<D>::V_TILE * sizeof(uint16_t);
+}
+
+template <class DT, int D, bool PAGED, bool XS>
+const void* balanced_kernel(const Plan& pl) {
+  return pl.wph > 1
+             ? reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, true>)
+             : reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false>);
+}
+
 template <int D, bool PAGED, bool XS>
 size_t balanced_lds(const Params& prm, const Plan& pl) {
-  return (XS ? 0 : (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t)) +
+  return tiles_lds<D, XS>(pl) +
          (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
 }
 
@@ -939,11 +1012,12 @@ size_t balanced_lds(const Params& prm, const Plan& pl) {
 // sequences into more partials for the merge.
 template <class DT, int D, bool PAGED, bool XS>
 int balanced_grid(const Params& prm, const Plan& pl) {
-  const void* kern = reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS>);
+  const void* kern = balanced_kernel<DT, D, PAGED, XS>(pl);
   int cus = 0;
-  const int resident0 = resident_grid(kern, 64 * pl.hpw, balanced_lds<D, PAGED, XS>(prm, pl), &cus);
+  const int waves = pl.hpw * pl.wph;
+  const int resident0 = resident_grid(kern, 64 * waves, balanced_lds<D, PAGED, XS>(prm, pl), &cus);
   if (resident0 <= 0) return 0;
-  const int per_cu = std::max(1, (kWavesPerCu + pl.hpw - 1) / pl.hpw);
+  const int per_cu = std::max(1, (kWavesPerCu + waves - 1) / waves);
   const int resident = std::min(resident0, std::max(1, cus) * per_cu);
   const int64_t want =
       (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
@@ -967,12 +1041,10 @@ template <class DT, int D, bool PAGED, bool XS>
 gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStream_t stream) {
   Params local = prm;
   void* args[] = {&local};
-  const int block = 64 * pl.hpw;
-  const size_t tiles_lds = XS ? 0 : (size_t)pl.hpw * Geo<D>::V_TILE * sizeof(uint16_t);
+  const int block = 64 * pl.hpw * pl.wph;
   if (phases & 1) {
     if (pl.balanced) {
-      const void* kern =
-          reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS>);
+      const void* kern = balanced_kernel<DT, D, PAGED, XS>(pl);
       const int grid = balanced_grid<DT, D, PAGED, XS>(prm, pl);
       if (grid <= 0) return GQA_ERR_LAUNCH;
       if (hipLaunchKernel(kern, dim3(grid), dim3(block), args,
@@ -988,8 +1060,8 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       const void* kern =
           short_walks ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true>)
                       : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false>);
-      if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(block), args, tiles_lds, stream) !=
-          hipSuccess)
+      if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(block), args, tiles_lds<D, XS>(pl),
+                          stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     }
   }
@@ -1102,6 +1174,7 @@ gqa_status_t run(const Problem& pb) {
   prm.tq = pb.tq;
   prm.ncol = G * pb.tq;
   prm.hpw = pl.hpw;
+  prm.wph = pl.wph;
   prm.n_groups = pl.n_groups;
   prm.s_kv = pb.s_kv;
   prm.max_blocks = pb.max_blocks;
