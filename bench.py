@@ -41,8 +41,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: line comments and whitespace are
+    dropped, so that a comment edit does not void recorded counters."""
+    with open(KERNEL_SRC) as f:
+        code = [line.split("//", 1)[0].split() for line in f]
+    return hashlib.sha256(" ".join(t for line in code for t in line).encode()).hexdigest()[:16]
 
 
 # ------------------------------------------------------------------ timing --

@@ -1,27 +1,28 @@
 // Single-query GQA decode attention for MI355X (gfx950, CDNA4).
 //
 // Kernels:
-//   partition kernels  a workgroup holds one wave per KV head of a head group
-//                      (HPW heads, up to 8); all its waves walk the same token
-//                      segment of one sequence, so that together they read
-//                      whole K/V rows (the cache interleaves the KV heads of
-//                      a token).  Each wave computes, for its KV head, the
-//                      partial triple (m, l, O) of the G query heads sharing
-//                      it (decode-long page, "Local attention" tile sweep and
-//                      "_merge_running") and either stores the normalised
-//                      output (the segment is the whole sequence; kernel-map
-//                      page, "paged_attention_v1") or the fp32 partial
-//                      (kernel-map page, "paged_attention_v2").  Two
-//                      schedulers feed them: fixed partitions (one workgroup
-//                      each) and a balanced persistent grid.
+//   partition kernels  a workgroup holds the waves of a head group of HPW KV
+//                      heads (up to 8, up to 4 at d = 256; a group of one or
+//                      two heads gets several waves per head); all its waves
+//                      walk the same token segment of one sequence, so that
+//                      together they read whole K/V rows (the cache
+//                      interleaves the KV heads of a token).  For its KV head
+//                      a wave computes the partial triple (m, l, O) of the
+//                      G * T_q query rows sharing it (decode-long page, "Local
+//                      attention" tile sweep and "_merge_running") and either
+//                      stores the normalised output (the segment is the whole
+//                      sequence; kernel-map page, "paged_attention_v1") or
+//                      the fp32 partial (kernel-map page, "paged_attention_v2").
+//                      Two schedulers feed them: fixed partitions (one
+//                      workgroup each) and a balanced persistent grid.
 //   merge kernels      1 to 64 slots of 16 lanes per (sequence, query head)
 //                      of a split sequence: the n-ary form of
 //                      "_merge_running" over the partials, then the
 //                      decode-long page's "Final normalise + store".
 //
-// Matrix-core mapping (v_mfma_f32_16x16x32_{f16,bf16}, wave64).  The G <= 16
-// query heads of one KV head are the 16-wide N side of both products, padded
-// with zero query rows:
+// Matrix-core mapping (v_mfma_f32_16x16x32_{f16,bf16}, wave64).  The G * T_q
+// <= 16 query rows of one KV head are the 16-wide N side of both products,
+// padded with zero query rows:
 //   S^T[16 tok x 16 head] += K[16 tok x 32 d] . Q^T[32 d x 16 head]
 //   O^T[16 d x 16 head]   += V^T[16 d x 32 tok] . P^T[32 tok x 16 head]
 // With this orientation every lane owns one head column (lane % 16) in both
@@ -29,9 +30,11 @@
 // head never leaves its lane group; only the tile max is exchanged between
 // the four 16-lane groups.  K feeds the A operand straight from HBM with
 // 16-byte loads (8 consecutive d of one token per lane).  V needs tokens
-// along the operand's K side, so each wave stages its V tile in LDS with
-// coalesced 16-byte stores and reads it back transposed.  Every wave keeps
-// the next tile's K and V loads in flight while it computes the current one.
+// along the operand's K side, so with the row layouts each wave stages its V
+// tile in LDS with coalesced 16-byte stores and reads it back transposed (the
+// x-split layout stores V transposed already).  Up to d = 128 every wave
+// keeps the next tile's K and V loads in flight while it computes the current
+// one.  K and V are read once, with non-temporal loads.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -198,10 +201,10 @@ struct Geo {
 // G heads each, every one attending to all L_s keys) and either stores the
 // normalised output (complete == true: the segment is the whole sequence) or
 // the fp32 partial at pml[c * ml_stride], po[c * o_stride] for column
-// c = tau * G + g.  The
-// wave walks its 32-token tiles in order and keeps the next tile's K and V
-// loads in flight while it computes the current one.  vt is the wave's LDS
-// tile (unused with XS).
+// c = tau * G + g.  The wave walks its 32-token tiles in order.  vt is the
+// wave's LDS tile inside smem (V staging with the row layouts; the sub-wave
+// state exchange with SPLIT), mlx the workgroup's (m, l) exchange (SPLIT).
+// NT selects non-temporal K/V loads.
 //
 // XS selects the x-split paged cache (kernel-map page, "paged_attention_v1",
 // the key_cache layout [num_blocks, h_kv, d / x, block_size, x] with x = 8

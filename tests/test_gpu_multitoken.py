@@ -94,3 +94,32 @@ def test_multitoken_unsupported_width(gq):
     with pytest.raises(gq.GqaError) as e:
         run_case(dev)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("layout", ["xsplit", "contiguous"])
+def test_multitoken_graph_replay(gq, layout):
+    """T_q = 2 steps captured in a HIP graph: every replay equals the eager result."""
+    case = _case(layout, 4, 2, 2, 128, W.F16, 3400)
+    dev = case_to_device(case, DEV)
+    stream = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(stream):
+        out = torch.empty_like(dev["q"])
+        kw = ({} if layout == "contiguous" else
+              dict(block_table=dev["block_table"], ctx_lens=dev["ctx_lens"]))
+        call = gq.prepare(dev["q"], dev["k"], dev["v"], scale=case.scale, out=out,
+                          policy=gq.policy_default(v1_max_ctx=0), stream=stream,
+                          xsplit=layout == "xsplit", **kw)
+        call(phases=3)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            call(phases=3)
+        for rep in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {rep}"
+    assert_close(eager.float().cpu().numpy().astype(np.float64), R.decode(case), W.F16,
+                 what=f"graph T_q=2 {layout}")
