@@ -175,14 +175,12 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
         # each; includes each launch's dispatch, so it reads above pass 1.
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda._sleep(spin)
-        t1 = time.perf_counter()
         for i in range(steps):
             kk, vv = ks[(warmup + i) % copies], vs[(warmup + i) % copies]
             evs[i][0].record(stream)
             call(kk, vv, phases=3)
             evs[i][1].record(stream)
         torch.cuda.synchronize()
-        eager_wall = (time.perf_counter() - t1) / steps
     step_ev = sorted(e[0].elapsed_time(e[1]) for e in evs)
     res = {"workload": case.name, "policy": policy_name,
            "partition_size": pol.partition_size, "v1_max_ctx": pol.v1_max_ctx,
@@ -190,7 +188,6 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
            "ms_per_step": wall * 1e3, "us_per_step": wall * 1e6,
            "us_per_step_gpu": gpu_step * 1e6,
            "gbs": case.kv_bytes / wall / 1e9,
-           "eager_us_per_step": eager_wall * 1e6,
            "partition_us_mean": mean_part * 1e3,
            "merge_us_mean": mean_merge * 1e3,
            "step_us_events_median": step_ev[len(step_ev) // 2] * 1e3,
@@ -406,7 +403,6 @@ def main():
                   "kernel times: HIP events around the steps' partition (then merge) "
                   "launches issued back to back; step_us_events: events around each "
                   "eager step, dispatch included",
-        "eager_us_per_step": round(head["eager_us_per_step"], 2),
         "step_us_events": {"median": round(head["step_us_events_median"], 2),
                            "p10": round(head["step_us_events_p10"], 2),
                            "p90": round(head["step_us_events_p90"], 2)},
