@@ -1,0 +1,45 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract and the kernel
+source hash that keys recorded counters."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) {\n  return x + 1;  // add one\n}\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    h0 = bench.source_hash()
+    src.write_text("// a header comment\nint  f(int x) {\n\n  return x + 1;\n}\n")
+    assert bench.source_hash() == h0
+    src.write_text("int f(int x) {\n  return x + 2;\n}\n")
+    assert bench.source_hash() != h0
+
+
+def test_traffic_record_requires_matching_source(tmp_path, monkeypatch):
+    import json
+    table = tmp_path / "traffic.json"
+    table.write_text(json.dumps({"w/default": {"source_sha": "nope", "bytes_per_launch": 1.0,
+                                               "partition_avg_ns": 1000.0}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(table))
+    assert bench.traffic_for("w", "default") == (None, None)
+    table.write_text(json.dumps({"w/default": {"source_sha": bench.source_hash(),
+                                               "bytes_per_launch": 5.0,
+                                               "partition_avg_ns": 2500.0}}))
+    assert bench.traffic_for("w", "default") == (5.0, 2.5)
+
+
+def test_bench_workloads_build_names():
+    assert "contig_b8" in bench.BENCH_WORKLOADS
+    assert bench.bench_desc("paged_b64_xsplit").endswith("x-split pool layout")
