@@ -674,26 +674,32 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
     const int64_t re = rs + nt;
     const int r = s * a.n_groups + hg;
     const int j = hg * a.hpw + (SPLIT ? w % a.hpw : w);
+    // This workgroup's part of the range: nothing (an unsplit range it does not
+    // own), the whole range (written directly), or one segment of a split range
+    // (a partial).  One call site keeps a single copy of the segment code.
+    bool run = true, complete = true;
+    int t0 = 0, t1 = L, slot = 0;
     if (L <= a.v1_max_ctx) {
-      if (rs >= x0) {                            // owned: the whole range, never split
-        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, 0, L, true, nullptr, 0, nullptr, 0);
-        if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
-      }
+      run = rs >= x0;                            // never split: owned by its first tile's share
     } else {
       const int64_t sa = max(rs, x0) - rs;
       const int64_t sb = min(re, x1) - rs;
-      const int t0 = (int)(sa * kTile);
-      const int t1 = (int)min(sb * kTile, (int64_t)L);
-      if (sa == 0 && sb == nt) {
-        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, true, nullptr, 0, nullptr, 0);
-        if (threadIdx.x == 0 && a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
-      } else {
-        const int slot = 2 * wg + (rs <= x0 ? 0 : 1);
-        const int64_t hrow = (int64_t)slot * heads + (SPLIT ? w % a.hpw : w) * a.ncol;
-        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, false, a.part_ml + hrow, 1,
-                                   a.part_o + hrow * D, D);
-        if (sa == 0 && threadIdx.x == 0)
+      t0 = (int)(sa * kTile);
+      t1 = (int)min(sb * kTile, (int64_t)L);
+      complete = sa == 0 && sb == nt;
+      slot = 2 * wg + (rs <= x0 ? 0 : 1);
+    }
+    if (run) {
+      const int64_t hrow = (int64_t)slot * heads + (SPLIT ? w % a.hpw : w) * a.ncol;
+      wave_segment<DT, D, PAGED, XS, true, SPLIT>(
+          a, smem, vt, mlx, s, j, t0, t1, complete, complete ? nullptr : a.part_ml + hrow, 1,
+          complete ? nullptr : a.part_o + hrow * D, D);
+      if (threadIdx.x == 0) {
+        if (complete) {
+          if (a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
+        } else if (t0 == 0) {
           a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
+        }
       }
     }
     if (++hg == a.n_groups) {
