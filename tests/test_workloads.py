@@ -60,3 +60,33 @@ def test_named_workloads_small_and_lengths():
     assert L5.min() >= 64 and L5.max() <= 32768
     assert (L5 > 8192).any() and (L5 <= 8192).any()     # both single pass and split fire
     assert np.array_equal(L5, W.lognormal_lengths(1004, 256, 2048.0, 1.0, 64, 32768))
+
+
+def test_xsplit_case_is_a_rearrangement():
+    rows = W.paged_case("xr", 5, [20, 3, 16], h_q=4, h_kv=2, d=16, dtype=W.F16,
+                        block_size=16, extra_blocks=1)
+    xs = W.xsplit_case(rows)
+    nb, bs, h_kv, d = rows.k.shape
+    assert xs.layout == "paged_xsplit"
+    assert xs.k.shape == (nb, h_kv, d // 8, bs, 8) and xs.v.shape == (nb, h_kv, d, bs)
+    for b in range(nb):
+        for o in range(bs):
+            for j in range(h_kv):
+                for dd in range(d):
+                    assert xs.k[b, j, dd // 8, o, dd % 8] == rows.k[b, o, j, dd]
+                    assert xs.v[b, j, dd, o] == rows.v[b, o, j, dd]
+    # poison moves with its slot: sequence 0's last block holds 4 live slots of 16
+    b = rows.block_table[0, 1]
+    assert np.all(xs.k[b, :, :, 4:, :] == W.NAN_BITS[W.F16])
+    assert np.all(xs.v[b, :, :, 4:] == W.NAN_BITS[W.F16])
+    assert np.array_equal(xs.q, rows.q) and np.array_equal(xs.block_table, rows.block_table)
+
+
+def test_multi_token_query_shape():
+    c = W.paged_case("mt", 6, [10, 40], h_q=8, h_kv=2, d=64, dtype=W.BF16, t_q=3)
+    assert c.q.shape == (2, 3, 8, 64) and c.t_q == 3
+    one = W.paged_case("mt1", 6, [10, 40], h_q=8, h_kv=2, d=64, dtype=W.BF16)
+    assert one.q.shape == (2, 8, 64) and one.t_q == 1
+    assert np.array_equal(c.k, one.k) and np.array_equal(c.v, one.v)   # K/V streams independent of q
+    cc = W.contiguous_case("mtc", 7, 2, 4, 1, 64, 33, W.F16, t_q=2)
+    assert cc.q.shape == (2, 2, 4, 64)
