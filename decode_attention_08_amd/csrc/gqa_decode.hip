@@ -725,6 +725,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
 
 constexpr int kMergeLanes = 16;                   // lanes per slot
 constexpr int kMergeUnroll = 8;                   // partials in flight per slot
+constexpr int kMergeSliceBelowBlocks = 256;       // slice d when the merge has fewer workgroups
 
 // 256 threads, or one head of SPI slots when that is larger (SPI = 64: 1024)
 __host__ __device__ constexpr int merge_block(int spi) {
@@ -734,20 +735,30 @@ __host__ __device__ constexpr int merge_heads_per_block(int spi) {
   return merge_block(spi) / (kMergeLanes * spi);
 }
 
-template <class DT, int D, bool PAGED, bool BALANCED, int SPI>
+// SLICED: a head's d is cut into D / 32 slices of 32, each merged by its own
+// slots (every slice reads all partials' (m, l), and its 128 bytes of each O
+// row).  It multiplies the workgroups of a merge with few heads and many
+// partials, whose reads would otherwise crowd onto few CUs.
+template <class DT, int D, bool PAGED, bool BALANCED, int SPI, bool SLICED>
 __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
-  constexpr int E = D / kMergeLanes;              // floats per lane: d / 16
+  constexpr int NSL = SLICED ? D / 32 : 1;        // d slices per head
+  constexpr int DS = D / NSL;                     // d per slice
+  constexpr int E = DS / kMergeLanes;             // floats per lane: 2, 4, 8 or 16
+  constexpr int VE = E < 4 ? E : 4;               // floats per load
+  typedef float vecE_t __attribute__((ext_vector_type(VE)));
   // a 1024-thread block leaves 128 registers per lane: fewer loads in flight at d = 256
-  constexpr int U = (merge_block(SPI) > 256 && D > 128) ? kMergeUnroll / 2 : kMergeUnroll;
+  constexpr int U = (merge_block(SPI) > 256 && E > 8) ? kMergeUnroll / 2 : kMergeUnroll;
   constexpr int SLOTS = merge_block(SPI) / kMergeLanes;
   constexpr int HPB = merge_heads_per_block(SPI);
-  static_assert(E % 4 == 0 && HPB >= 1 && HPB * SPI == SLOTS, "merge shape");
+  static_assert(E % 2 == 0 && HPB >= 1 && HPB * SPI == SLOTS, "merge shape");
   const int slot = threadIdx.x / kMergeLanes;
   const int r = threadIdx.x % kMergeLanes;
   const int sub = slot % SPI;                     // subset of the partials
   // one output row: (sequence s, query token tau, query head i) = item, the
-  // row-major index of out[num_seqs, T_q, h_q]
-  const int item = blockIdx.x * HPB + slot / SPI;
+  // row-major index of out[num_seqs, T_q, h_q]; slice: its d range
+  const int vitem = blockIdx.x * HPB + slot / SPI;
+  const int item = vitem / NSL;
+  const int d0 = (vitem % NSL) * DS;
   const int heads = a.hpw * a.ncol;               // partial rows per balanced slot
   // ---- the partial rows of this head; n = 0 for a head written in one pass.
   // No early return: with SPI > 1 every slot reaches the barrier below.
@@ -784,15 +795,15 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   for (int k0 = sub; k0 < n; k0 += U * SPI) {
     float2 t2[U];
-    float4_t v[U][E / 4];
+    vecE_t v[U][E / VE];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (k0 + u * SPI < n) {
         const int64_t rw = row(k0 + u * SPI);
         t2[u] = a.part_ml[rw];
-        const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + r * E);
+        const vecE_t* src = reinterpret_cast<const vecE_t*>(a.part_o + rw * D + d0 + r * E);
 #pragma unroll
-        for (int e4 = 0; e4 < E / 4; ++e4) v[u][e4] = src[e4];
+        for (int e4 = 0; e4 < E / VE; ++e4) v[u][e4] = src[e4];
       }
     }
 #pragma unroll
@@ -803,34 +814,30 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
         const float a_new = __builtin_amdgcn_exp2f(t2[u].x - m_new);
         l = l * a_old + t2[u].y * a_new;
 #pragma unroll
-        for (int e4 = 0; e4 < E / 4; ++e4)
+        for (int e4 = 0; e4 < E / VE; ++e4)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) o[4 * e4 + c] = o[4 * e4 + c] * a_old + v[u][e4][c] * a_new;
+          for (int c = 0; c < VE; ++c)
+            o[VE * e4 + c] = o[VE * e4 + c] * a_old + v[u][e4][c] * a_new;
         m = m_new;
       }
     }
   }
-  uint16_t* dst = a.out + (int64_t)item * D;
+  uint16_t* dst = a.out + (int64_t)item * D + d0;
   if constexpr (SPI == 1) {
     if (n > 0) {
       uint32_t packed[E / 2];
 #pragma unroll
       for (int e2 = 0; e2 < E / 2; ++e2)
         packed[e2] = DT::narrow(o[2 * e2] / l) | (DT::narrow(o[2 * e2 + 1] / l) << 16);
-      if constexpr (E == 8)
-        *reinterpret_cast<uint4_t*>(dst + r * E) =
-            uint4_t{packed[0], packed[1], packed[2], packed[3]};
-      else
-        *reinterpret_cast<uint2*>(dst + r * E) = uint2{packed[0], packed[1]};
+#pragma unroll
+      for (int e2 = 0; e2 < E / 2; ++e2) reinterpret_cast<uint32_t*>(dst + r * E)[e2] = packed[e2];
     }
   } else {
-    // ---- combine the SPI slot results of each head in slot order
-    __shared__ float red_o[SLOTS][D];
+    // ---- combine the SPI slot results of each head slice in slot order
+    __shared__ float red_o[SLOTS][DS];
     __shared__ float red_m[SLOTS], red_l[SLOTS];
 #pragma unroll
-    for (int e4 = 0; e4 < E / 4; ++e4)
-      *reinterpret_cast<float4_t*>(&red_o[slot][r * E + 4 * e4]) =
-          float4_t{o[4 * e4], o[4 * e4 + 1], o[4 * e4 + 2], o[4 * e4 + 3]};
+    for (int e = 0; e < E; ++e) red_o[slot][r * E + e] = o[e];
     if (r == 0) red_m[slot] = m;
     __syncthreads();
     const int first = slot - sub;                 // the head's first slot
@@ -849,7 +856,7 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
     if (n > 0) {
       float lsum = 0.f;
       for (int u = 0; u < SPI; ++u) lsum += red_l[first + u];
-      for (int c = sub * kMergeLanes + r; c < D; c += SPI * kMergeLanes) {
+      for (int c = sub * kMergeLanes + r; c < DS; c += SPI * kMergeLanes) {
         float acc = 0.f;
         for (int u = 0; u < SPI; ++u) acc += red_o[first + u][c] * red_m[first + u];
         dst[c] = DT::narrow(acc / lsum);
@@ -1033,13 +1040,14 @@ int balanced_grid(const Params& prm, const Plan& pl) {
   return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxGrid, resident, want}));
 }
 
-template <class DT, int D, bool PAGED, int SPI>
+template <class DT, int D, bool PAGED, int SPI, bool SLICED>
 gqa_status_t launch_merge(bool balanced, int64_t items, void** args, hipStream_t stream) {
-  const void* kern = balanced
-                         ? reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, true, SPI>)
-                         : reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, false, SPI>);
+  const void* kern =
+      balanced ? reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, true, SPI, SLICED>)
+               : reinterpret_cast<const void*>(&merge_kernel<DT, D, PAGED, false, SPI, SLICED>);
   constexpr int per_block = merge_heads_per_block(SPI);
-  const int64_t grid = (items + per_block - 1) / per_block;
+  const int64_t vitems = items * (SLICED ? D / 32 : 1);
+  const int64_t grid = (vitems + per_block - 1) / per_block;
   if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(merge_block(SPI)), args, 0, stream) !=
       hipSuccess)
     return GQA_ERR_LAUNCH;
@@ -1091,12 +1099,22 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
     int spi = 1;
     while (spi < 16 && (per_head > 2 * kMergeUnroll * spi || items * spi < 4096)) spi *= 4;
     if (per_head > 16 * 4 * kMergeUnroll) spi = 64;
+    // Few heads with many partials would leave most CUs idle: cut each head's
+    // d into slices of 32 when the unsliced grid has fewer workgroups than CUs.
+    const int64_t blocks = (items + merge_heads_per_block(spi) - 1) / merge_heads_per_block(spi);
+    const bool sliced = spi >= 16 && blocks < kMergeSliceBelowBlocks;
     gqa_status_t st;
     switch (spi) {
-      case 1: st = launch_merge<DT, D, PAGED, 1>(pl.balanced, items, args, stream); break;
-      case 4: st = launch_merge<DT, D, PAGED, 4>(pl.balanced, items, args, stream); break;
-      case 16: st = launch_merge<DT, D, PAGED, 16>(pl.balanced, items, args, stream); break;
-      default: st = launch_merge<DT, D, PAGED, 64>(pl.balanced, items, args, stream); break;
+      case 1: st = launch_merge<DT, D, PAGED, 1, false>(pl.balanced, items, args, stream); break;
+      case 4: st = launch_merge<DT, D, PAGED, 4, false>(pl.balanced, items, args, stream); break;
+      case 16:
+        st = sliced ? launch_merge<DT, D, PAGED, 16, true>(pl.balanced, items, args, stream)
+                    : launch_merge<DT, D, PAGED, 16, false>(pl.balanced, items, args, stream);
+        break;
+      default:
+        st = sliced ? launch_merge<DT, D, PAGED, 64, true>(pl.balanced, items, args, stream)
+                    : launch_merge<DT, D, PAGED, 64, false>(pl.balanced, items, args, stream);
+        break;
     }
     if (st != GQA_OK) return st;
   }

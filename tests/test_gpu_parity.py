@@ -282,7 +282,8 @@ def test_graph_replay_matches_eager(gq, pname):
 
 def _merge_case(kind):
     """Fixed 32-token partitions shaped so that the merge runs 1, 4, 16 and 64
-    slots per head: (heads, partials per head) = (4200, 16), (1200, 64), (64, 200), (16, 625)."""
+    slots per head: (heads, partials per head) = (4200, 16), (1200, 64), (64, 200),
+    (16, 625); the last two with d sliced (few merge blocks), and (256, 625) unsliced."""
     rng = np.random.default_rng(1600)
     if kind == "slots1":
         lens = rng.integers(0, 513, size=2100)
@@ -295,10 +296,14 @@ def _merge_case(kind):
     if kind == "slots16":
         return W.paged_case(kind, 1603, [6400, 3000, 31, 0], h_q=16, h_kv=2, d=128,
                             dtype=W.BF16, extra_blocks=1)
+    if kind == "slots64_unsliced":                 # 256 heads x 625 partials: 256 merge blocks
+        lens = rng.integers(1, 20001, size=16)
+        lens[0] = 20000
+        return W.paged_case(kind, 1605, lens, h_q=16, h_kv=2, d=64, dtype=W.BF16)
     return W.paged_case(kind, 1604, [20000, 777], h_q=8, h_kv=1, d=128, dtype=W.F16)
 
 
-@pytest.mark.parametrize("kind", ["slots1", "slots4", "slots16", "slots64"])
+@pytest.mark.parametrize("kind", ["slots1", "slots4", "slots16", "slots64", "slots64_unsliced"])
 def test_merge_widths(gq, kind):
     case = _merge_case(kind)
     heads = [(s, i) for s in range(min(case.num_seqs, 40)) for i in range(case.h_q)]
