@@ -322,3 +322,27 @@ def test_balanced_merge_spread(gq, nseq):
     heads = [(s, i) for s in range(min(nseq, 4)) for i in range(32)]
     got = run_case(case_to_device(case, DEV), policy=gq.policy_default(v1_max_ctx=0))
     assert_close(got, R.decode(case, heads=heads), W.F16, what=f"balanced nseq={nseq}")
+
+
+def test_concurrent_streams(gq):
+    """Calls on two streams with their own workspaces and outputs may overlap."""
+    a = W.paged_case("cs_a", 1800, [5000, 300, 9000], h_q=32, h_kv=8, d=128, dtype=W.F16)
+    b = W.contiguous_case("cs_b", 1801, 4, 16, 4, 64, 3000, W.BF16)
+    da, db = case_to_device(a, DEV), case_to_device(b, DEV)
+    want_a, want_b = run_case(da), run_case(db)
+    sa, sb = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    outs = []
+    for _ in range(3):
+        oa, ob = torch.empty_like(da["q"]), torch.empty_like(db["q"])
+        ca = gq.prepare(da["q"], da["k"], da["v"], block_table=da["block_table"],
+                        ctx_lens=da["ctx_lens"], scale=a.scale, out=oa, stream=sa)
+        cb = gq.prepare(db["q"], db["k"], db["v"], scale=b.scale, out=ob, stream=sb)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            ca()
+            cb()
+        torch.cuda.synchronize()
+        outs.append((oa, ob))
+    for oa, ob in outs:
+        assert np.array_equal(oa.float().cpu().numpy().astype(np.float64), want_a)
+        assert np.array_equal(ob.float().cpu().numpy().astype(np.float64), want_b)
