@@ -69,6 +69,7 @@ def _spin_cycles(torch, stream, seconds: float) -> int:
 
 
 XSPLIT_SUFFIX = "_xsplit"
+FUSED_ROWS = ("contig_b8", "paged_b64", "long_128k", "mixed_b256")   # also timed with the fused merge
 BENCH_WORKLOADS = ["tiny_contig", "contig_b8", "paged_b64", "long_128k", "mixed_b256",
                    "contig_d256", "paged_b64_t4", "paged_b64_xsplit", "mixed_b256_xsplit"]
 
@@ -104,7 +105,9 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     from tests.parity import bits_to_device
 
     dev = torch.device("cuda:0")
-    pol = gq.policy_default() if policy_name == "default" else gq.policy_pages()
+    pol = {"default": gq.policy_default,
+           "pages": gq.policy_pages,
+           "fused": lambda: gq.policy_default(flags=gq.GQA_POLICY_FUSED_MERGE)}[policy_name]()
     q = bits_to_device(case.q, case.dtype, dev)
     k0 = bits_to_device(case.k, case.dtype, dev)
     v0 = bits_to_device(case.v, case.dtype, dev)
@@ -314,7 +317,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--policy", default="default", choices=["default", "pages"])
+    ap.add_argument("--policy", default="default", choices=["default", "pages", "fused"])
     ap.add_argument("--no-also", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -365,10 +368,12 @@ def main():
     if not args.no_also:
         for name in BENCH_WORKLOADS:
             c = case if name == args.workload else bench_case(name)
-            for pol in ("default", "pages"):
+            for pol in ("default", "pages", "fused"):
                 if name == args.workload and pol == args.policy:
                     continue
                 if name.endswith(XSPLIT_SUFFIX) and pol != "default":
+                    continue
+                if pol == "fused" and name not in FUSED_ROWS:
                     continue
                 r = time_workload(c, pol, args.steps, args.warmup)
                 also[f"{name}/{pol}"] = {k: (round(v, 3) if isinstance(v, float) else v)

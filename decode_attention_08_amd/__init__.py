@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     GQA_KV_PAGED_XSPLIT,
     DecodeArgs,
     GQA_F16,
+    GQA_POLICY_FUSED_MERGE,
     GqaError,
     Policy,
     decode,

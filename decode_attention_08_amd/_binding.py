@@ -18,6 +18,7 @@ lib = ctypes.CDLL(library_path)
 
 GQA_F16 = 0
 GQA_BF16 = 1
+GQA_POLICY_FUSED_MERGE = 1
 
 GQA_KV_CONTIGUOUS = 0
 GQA_KV_PAGED = 1
@@ -30,13 +31,14 @@ X = 8   # elements per 16-byte vector of the x-split K layout
 
 
 class Policy(ctypes.Structure):
-    """gqa_policy_t: partition_size, v1_max_ctx, phases (0/3 both, 1 partition, 2 merge)."""
+    """gqa_policy_t: partition_size, v1_max_ctx, phases (0/3 both, 1 partition, 2 merge),
+    flags (0 or GQA_POLICY_FUSED_MERGE)."""
     _fields_ = [("partition_size", ctypes.c_int32), ("v1_max_ctx", ctypes.c_int32),
-                ("phases", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("phases", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"Policy(partition_size={self.partition_size}, v1_max_ctx={self.v1_max_ctx}, "
-                f"phases={self.phases})")
+                f"phases={self.phases}, flags={self.flags})")
 
 
 class DecodeArgs(ctypes.Structure):
@@ -145,11 +147,14 @@ def _out(q, out):
     return out
 
 
-def _workspace(workspace, need, device):
+def _workspace(workspace, need, device, zeroed: bool = False):
+    """The caller's workspace, or a new one (zero-filled when the policy's fused
+    merge needs its counters at zero before the first call)."""
     if need == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        alloc = torch.zeros if zeroed else torch.empty
+        workspace = alloc(need, dtype=torch.uint8, device=device)
     _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
     return workspace, workspace.numel() * workspace.element_size()
 
@@ -205,7 +210,7 @@ class PreparedCall:
     """
 
     def __init__(self, layout: int, args: DecodeArgs, policy: Policy, keep):
-        self._policy = Policy(policy.partition_size, policy.v1_max_ctx, policy.phases, 0)
+        self._policy = Policy(policy.partition_size, policy.v1_max_ctx, policy.phases, policy.flags)
         self._a = args
         self._a.policy = ctypes.pointer(self._policy)
         self._layout = layout
@@ -264,7 +269,8 @@ def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
                    stream=_stream(stream, q.device))
     a.policy = ctypes.pointer(policy)
     need = int(lib.gqa_decode_ex_workspace_size(ctypes.byref(a)))
-    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device,
+                                     zeroed=bool(policy.flags & GQA_POLICY_FUSED_MERGE))
     a.workspace = _ptr(workspace)
     a.workspace_bytes = ws_bytes
     return PreparedCall(layout, a, policy, (q, k, v, block_table, ctx_lens, out, workspace))

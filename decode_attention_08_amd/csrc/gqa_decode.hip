@@ -112,6 +112,7 @@ struct Params {
   float2* part_ml;              // partial (m in log2 units, l) per (slot, query head)
   float* part_o;                // partial un-normalised O row per (slot, query head)
   int4* desc;                   // balanced mode: per (sequence, head group) segment record
+  int* cnt;                     // fused merge: segments finished per (sequence, head group)
   int num_seqs;
   int h_q;
   int h_kv;
@@ -577,6 +578,69 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
       (int64_t)a.max_parts * D);
 }
 
+// --------------------------------------------------------- fused merge --
+//
+// The workgroup that finished a split range last merges it (policy flag
+// GQA_POLICY_FUSED_MERGE): the n-ary "_merge_running" of the decode-long page
+// over the range's n segments, in segment order, then "Final normalise +
+// store".  One 16-lane slot per partial row (a query row of the head group);
+// lane r holds d elements [r*D/16, (r+1)*D/16).  Partial k of the range sits
+// in slot `first` (k = 0) or 2 (wg0 + k), as the balanced kernel wrote it.
+
+template <class DT, int D>
+__device__ __forceinline__ void fused_range_merge(const Params& a, int s, int hg, int wg0, int n,
+                                                  int first) {
+  constexpr int E = D / 16;
+  constexpr int U = 8;
+  const int heads = a.hpw * a.ncol;               // partial rows per slot
+  const int nslot = blockDim.x / 16;
+  const int r = threadIdx.x % 16;
+  for (int row = threadIdx.x / 16; row < heads; row += nslot) {
+    float m = -INFINITY, l = 0.f;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+    for (int k0 = 0; k0 < n; k0 += U) {
+      float2 t2[U];
+      float4_t v[U][E / 4];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u < n) {
+          const int k = k0 + u;
+          const int64_t rw = (int64_t)(k == 0 ? first : 2 * (wg0 + k)) * heads + row;
+          t2[u] = a.part_ml[rw];
+          const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + r * E);
+#pragma unroll
+          for (int e4 = 0; e4 < E / 4; ++e4) v[u][e4] = src[e4];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u < n) {
+          const float m_new = fmaxf(m, t2[u].x);  // finite: a partial holds at least one token
+          const float a_old = __builtin_amdgcn_exp2f(m - m_new);
+          const float a_new = __builtin_amdgcn_exp2f(t2[u].x - m_new);
+          l = l * a_old + t2[u].y * a_new;
+#pragma unroll
+          for (int e4 = 0; e4 < E / 4; ++e4)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              o[4 * e4 + c] = o[4 * e4 + c] * a_old + v[u][e4][c] * a_new;
+          m = m_new;
+        }
+      }
+    }
+    // partial row -> output row: KV head j = hg * hpw + row / ncol, column c = tau * G + g
+    const int c = row % a.ncol;
+    const int j = hg * a.hpw + row / a.ncol;
+    uint16_t* dst = a.out + (((int64_t)s * a.tq + c / a.group) * a.h_q + j * a.group + c % a.group) * D;
+#pragma unroll
+    for (int e2 = 0; e2 < E / 2; ++e2)
+      reinterpret_cast<uint32_t*>(dst + r * E)[e2] =
+          DT::narrow(o[2 * e2] / l) | (DT::narrow(o[2 * e2 + 1] / l) << 16);
+  }
+}
+
 // ------------------------------------------------------- balanced kernel --
 //
 // Persistent grid of W workgroups.  The (sequence, head group) ranges are
@@ -602,11 +666,12 @@ __device__ __forceinline__ int64_t range_prefix(const Params& a, const int32_t* 
     return (int64_t)s * a.n_groups * seq_tiles(a.s_kv);
 }
 
-template <class DT, int D, bool PAGED, bool XS, bool SPLIT>
+template <class DT, int D, bool PAGED, bool XS, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balanced_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // wave tiles, then the prefix
   __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
   __shared__ float2 mlx[kMaxHeadsPerGroup * 16];                     // sub-wave (m, l) exchange
+  __shared__ int last_of_range;                                      // fused merge
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;                // = hpw * wph
@@ -700,6 +765,31 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
         } else if (t0 == 0) {
           a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
         }
+      }
+      if (FUSED && !complete) {
+        // Fused merge.  Release this workgroup's partials, count it in, and let
+        // the workgroup that completes the count merge the range; it resets
+        // the counter for the next call.  Nothing waits on other workgroups.
+        // The barrier orders every wave's partial stores before thread 0's
+        // device-scope release, and thread 0's acquire before every wave's
+        // reads; one fence per workgroup matters, since on this part a
+        // device-scope fence writes back (release) or invalidates (acquire)
+        // the whole L2 of the XCD.
+        const int wg0 = (int)(rs / chunk);       // the range's first and last shares
+        const int n = (int)((re - 1) / chunk) - wg0 + 1;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          __threadfence();
+          last_of_range = atomicAdd(a.cnt + r, 1) == n - 1;
+          if (last_of_range) __threadfence();
+        }
+        __syncthreads();
+        if (last_of_range) {
+          const int first = 2 * wg0 + (rs == (int64_t)wg0 * chunk ? 0 : 1);
+          fused_range_merge<DT, D>(a, s, hg, wg0, n, first);
+          if (threadIdx.x == 0) a.cnt[r] = 0;
+        }
+        __syncthreads();                         // last_of_range read before it is rewritten
       }
     }
     if (++hg == a.n_groups) {
@@ -906,7 +996,9 @@ gqa_status_t resolve_policy(const gqa_policy_t* in, gqa_policy_t* out) {
   const bool balanced = out->partition_size == 0;
   if ((!balanced && (out->partition_size < kTile || out->partition_size > (1 << 20) ||
                      out->partition_size % kTile != 0)) ||
-      out->v1_max_ctx < 0 || out->phases < 0 || out->phases > 3 || out->reserved != 0)
+      out->v1_max_ctx < 0 || out->phases < 0 || out->phases > 3 ||
+      (out->flags & ~GQA_POLICY_FUSED_MERGE) != 0 ||
+      ((out->flags & GQA_POLICY_FUSED_MERGE) && !balanced))
     return GQA_ERR_BAD_POLICY;
   if (out->phases == 0) out->phases = 3;
   return GQA_OK;
@@ -930,7 +1022,8 @@ struct Plan {
   int part_size;      // fixed mode
   int max_parts;      // fixed mode
   bool can_split;     // some sequence may exceed v1_max_ctx
-  size_t ws_desc, ws_ml, ws_o, ws_total;   // byte sizes of the workspace regions
+  bool fused;         // split ranges merged by their last workgroup (no merge kernel)
+  size_t ws_desc, ws_cnt, ws_ml, ws_o, ws_total;   // byte sizes of the workspace regions
 };
 
 int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
@@ -953,13 +1046,16 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
   // which split each segment's tiles: a lone wave per head walking a short
   // sequence is latency-bound.  Larger groups have waves enough; on a batch of
   // 256 sequences of ~3400 tokens with four KV heads the split cost 2%.
-  if (pl.balanced && pl.hpw <= 2) pl.wph = max_heads_per_group(d) / pl.hpw;
+  if (pl.balanced && pl.hpw <= 2 && !(pol.flags & GQA_POLICY_FUSED_MERGE))
+    pl.wph = max_heads_per_group(d) / pl.hpw;
   pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
   if (!pl.can_split) return pl;
   if (pl.balanced) {
     const size_t rows = (size_t)2 * kMaxGrid * pl.hpw * (h_q / h_kv) * t_q;
+    pl.fused = (pol.flags & GQA_POLICY_FUSED_MERGE) != 0;
     pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
+    pl.ws_cnt = pl.fused ? align256((size_t)num_seqs * pl.n_groups * sizeof(int)) : 0;
     pl.ws_ml = align256(rows * sizeof(float2));
     pl.ws_o = rows * (size_t)d * sizeof(float);
   } else {
@@ -968,7 +1064,7 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
     pl.ws_ml = align256(rows * sizeof(float2));
     pl.ws_o = rows * (size_t)d * sizeof(float);
   }
-  pl.ws_total = pl.ws_desc + pl.ws_ml + pl.ws_o;
+  pl.ws_total = pl.ws_desc + pl.ws_cnt + pl.ws_ml + pl.ws_o;
   return pl;
 }
 
@@ -1009,9 +1105,11 @@ size_t tiles_lds(const Plan& pl) {
 
 template <class DT, int D, bool PAGED, bool XS>
 const void* balanced_kernel(const Plan& pl) {
+  if (pl.fused)   // one wave per head (make_plan)
+    return reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false, true>);
   return pl.wph > 1
-             ? reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, true>)
-             : reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false>);
+             ? reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, true, false>)
+             : reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false, false>);
 }
 
 template <int D, bool PAGED, bool XS>
@@ -1082,7 +1180,7 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
         return GQA_ERR_LAUNCH;
     }
   }
-  if ((phases & 2) && pl.can_split) {
+  if ((phases & 2) && pl.can_split && !pl.fused) {
     // partials per split head: about grid / ranges for the balanced scheduler
     // (a range's tiles spread over that many shares), max_parts for fixed partitions
     int64_t per_head = pl.max_parts;
@@ -1191,8 +1289,9 @@ gqa_status_t run(const Problem& pb) {
   if (pl.ws_total > 0) {
     char* ws = static_cast<char*>(pb.ws);
     prm.desc = pl.ws_desc ? reinterpret_cast<int4*>(ws) : nullptr;
-    prm.part_ml = reinterpret_cast<float2*>(ws + pl.ws_desc);
-    prm.part_o = reinterpret_cast<float*>(ws + pl.ws_desc + pl.ws_ml);
+    prm.cnt = pl.ws_cnt ? reinterpret_cast<int*>(ws + pl.ws_desc) : nullptr;
+    prm.part_ml = reinterpret_cast<float2*>(ws + pl.ws_desc + pl.ws_cnt);
+    prm.part_o = reinterpret_cast<float*>(ws + pl.ws_desc + pl.ws_cnt + pl.ws_ml);
   }
   prm.num_seqs = pb.num_seqs;
   prm.h_q = pb.h_q;
@@ -1256,7 +1355,7 @@ void gqa_policy_default(gqa_policy_t* p) {
   p->partition_size = 0;
   p->v1_max_ctx = kDefaultV1Max;
   p->phases = 0;
-  p->reserved = 0;
+  p->flags = 0;
 }
 
 void gqa_policy_pages(gqa_policy_t* p) {
@@ -1264,7 +1363,7 @@ void gqa_policy_pages(gqa_policy_t* p) {
   p->partition_size = 512;
   p->v1_max_ctx = 8192;
   p->phases = 0;
-  p->reserved = 0;
+  p->flags = 0;
 }
 
 size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, int max_ctx,

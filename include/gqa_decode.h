@@ -103,12 +103,24 @@ typedef enum gqa_status {
  * workspace); it exists so that a caller can time the two kernels apart.
  * The balanced decomposition needs num_seqs <= 8192; a larger batch uses the
  * fixed one with 512-token partitions.
+ *
+ * flags: 0, or GQA_POLICY_FUSED_MERGE (balanced decomposition only; other
+ * bits are errors).  With it, the workgroup that finishes a split range last
+ * merges that range itself (it finds out through a per-range atomic counter in
+ * the workspace; nothing waits on anything), and no merge kernel is launched.
+ * It saves the merge launch, but a range's merge then runs on one CU, so it
+ * pays only for batches of many short split ranges.  Contract: the workspace
+ * must be zero-filled before its first call with this flag (for instance when
+ * it is allocated); every call that runs to completion leaves the counters at
+ * zero again, graph replays included.  phases 2 then does nothing.
  */
+#define GQA_POLICY_FUSED_MERGE 1
+
 typedef struct gqa_policy {
   int32_t partition_size;
   int32_t v1_max_ctx;
   int32_t phases;
-  int32_t reserved;        /* must be 0 */
+  int32_t flags;           /* 0 or GQA_POLICY_FUSED_MERGE */
 } gqa_policy_t;
 
 /* Fill *p with the MI355X default policy. */
@@ -120,8 +132,10 @@ void gqa_policy_pages(gqa_policy_t* p);
  * Bytes of workspace gqa_decode / gqa_decode_contiguous need for these sizes
  * (max_ctx = max_blocks_per_seq * block_size, or s_kv).  0 when no sequence
  * can be split.  The workspace holds fp32 partial triples (m, l, O) and, for
- * the balanced decomposition, one 16-byte record per (sequence, KV head); its
- * contents need no initialisation.  policy NULL means gqa_policy_default().
+ * the balanced decomposition, one 16-byte record per (sequence, head group)
+ * (plus one counter per (sequence, head group) with GQA_POLICY_FUSED_MERGE);
+ * its contents need no initialisation, except under GQA_POLICY_FUSED_MERGE
+ * (see gqa_policy_t).  policy NULL means gqa_policy_default().
  * Returns 0 for invalid arguments.
  */
 size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, int max_ctx,

@@ -130,7 +130,8 @@ def test_validation_errors(gq, kw, code, entry):
 def test_policy_and_workspace_errors(gq):
     for pol in (gq.Policy(100, 0, 0, 0), gq.Policy(16, 0, 0, 0), gq.Policy(-32, 0, 0, 0),
                 gq.Policy(512, -1, 0, 0), gq.Policy(0, -1, 0, 0), gq.Policy(512, 0, 4, 0),
-                gq.Policy(0, 0, -1, 0), gq.Policy(512, 0, 0, 1), gq.Policy(1 << 21, 0, 0, 0)):
+                gq.Policy(0, 0, -1, 0), gq.Policy(512, 0, 0, 1), gq.Policy(1 << 21, 0, 0, 0),
+                gq.Policy(0, 0, 0, 2), gq.Policy(0, 0, 0, -1)):
         assert _call(gq, policy=pol) == ERR["POLICY"], pol
         assert _call(gq, "gqa_decode_xsplit", policy=pol) == ERR["POLICY"], pol
     for pol in (gq.policy_pages(v1_max_ctx=0), gq.policy_default(v1_max_ctx=0)):
@@ -208,3 +209,14 @@ def test_ex_workspace_size(gq):
         gq.workspace_size(2, 8, 2, 128, 4096, B)
     assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(_ex(gq, t_q=0))) == 0
     assert gq.lib.gqa_decode_ex_workspace_size(None) == 0
+
+
+def test_fused_policy_workspace(gq):
+    """The fused merge adds one counter per (sequence, head group) after the records."""
+    B = gq.policy_default()
+    F = gq.policy_default(flags=gq.GQA_POLICY_FUSED_MERGE)
+    plain = gq.workspace_size(3, 32, 8, 128, 4096, B)
+    fused = gq.workspace_size(3, 32, 8, 128, 4096, F)
+    assert fused == plain + 256                                  # 3 counters, 256-aligned
+    assert gq.workspace_size(3, 32, 8, 128, 200, F) == 0         # nothing can split
+    assert gq.workspace_size(3, 32, 8, 128, 4096, gq.Policy(512, 8192, 0, 1)) == 0   # fixed: invalid
