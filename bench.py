@@ -234,18 +234,29 @@ def cpu_baseline(case, budget_s: float = 10.0):
             "seconds": round(t_used, 3)}
 
 
-def traffic_for(workload: str, policy: str):
-    """(HBM bytes per partition-kernel launch, rocprofv3 mean kernel duration in
-    us) recorded in profiles/, if taken on the current kernel source, else
-    (None, None)."""
+def _round(x, nd: int = 2):
+    return None if x is None else round(x, nd)
+
+
+def traffic_record(workload: str, policy: str) -> dict:
+    """The rocprofv3 record of profiles/traffic.json for this workload and
+    policy, if taken on the current kernel source, else {}."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None, None
+        return {}
     rec = t.get(f"{workload}/{policy}")
     if not rec or rec.get("source_sha") != source_hash():
-        return None, None
+        return {}
+    return rec
+
+
+def traffic_for(workload: str, policy: str):
+    """(HBM bytes per partition-kernel launch, rocprofv3 mean kernel duration in
+    us) recorded in profiles/, if taken on the current kernel source, else
+    (None, None)."""
+    rec = traffic_record(workload, policy)
     avg = rec.get("partition_avg_ns")
     return rec.get("bytes_per_launch"), (None if avg is None else round(avg * 1e-3, 3))
 
@@ -267,7 +278,8 @@ def summarize_rocprof(path: str, probe_bytes: int = 1 << 30):
 
     Expects `path`/trace (--kernel-trace --stats), `path`/fetch (--pmc
     FETCH_SIZE) and `path`/write (--pmc WRITE_SIZE), each made with
-    --copy-probe 1024 for the counter runs.  Counter values (KiB per dispatch)
+    --copy-probe 1024 for the counter runs, and optionally `path`/busy (--pmc
+    VALUBusy MfmaUtil).  Counter values (KiB per dispatch)
     are scaled by what the same counter reads for the 1 GiB probe copy (the
     largest copy dispatch of the run).  Returns (text, traffic record).
     """
@@ -303,6 +315,16 @@ def summarize_rocprof(path: str, probe_bytes: int = 1 << 30):
             if part and factor:
                 rec[counter] = {"kib_avg": sum(part) / len(part), "factor": factor,
                                 "bytes_per_launch": sum(part) / len(part) * 1024.0 * factor}
+    for db, con in _rocpd(path, "busy"):
+        lines.append(f"# counters VALUBusy, MfmaUtil (percent): {os.path.relpath(db, path)}")
+        rows = con.execute(
+            "select kernel_name, counter_name, avg(value), count(*) from counters_collection "
+            "where counter_name in ('VALUBusy', 'MfmaUtil') group by kernel_name, counter_name "
+            "order by kernel_name").fetchall()
+        for n, cname, v, c in rows:
+            lines.append(f"{_short(n):100s} {cname} avg={v:.2f}% dispatches={c}")
+            if "partition_" in n:
+                rec["valu_busy_pct" if cname == "VALUBusy" else "mfma_util_pct"] = v
     if "FETCH_SIZE" in rec and "WRITE_SIZE" in rec:
         rec["bytes_per_launch"] = rec["FETCH_SIZE"]["bytes_per_launch"] + rec["WRITE_SIZE"]["bytes_per_launch"]
     rec["source_sha"] = source_hash()
@@ -416,6 +438,8 @@ def main():
                      "traffic": traffic, "kernel": "partition_kernel",
                      "kernel_us_mean": round(head["partition_us_mean"], 3),
                      "kernel_us_rocprof": rocprof_us,
+                     "valu_busy_pct": _round(traffic_record(case.name, args.policy).get("valu_busy_pct")),
+                     "mfma_util_pct": _round(traffic_record(case.name, args.policy).get("mfma_util_pct")),
                      "merge_us_mean": round(head["merge_us_mean"], 3)},
         "cpu_baseline": cpu,
         "also": also,
