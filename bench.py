@@ -70,6 +70,8 @@ def _spin_cycles(torch, stream, seconds: float) -> int:
 
 XSPLIT_SUFFIX = "_xsplit"
 FUSED_ROWS = ("contig_b8", "paged_b64", "long_128k", "mixed_b256")   # also timed with the fused merge
+VALU_ROWS = FUSED_ROWS        # also timed with the products on the vector ALU (dot2)
+POLICIES = ("default", "pages", "fused", "valu")
 BENCH_WORKLOADS = ["tiny_contig", "contig_b8", "paged_b64", "long_128k", "mixed_b256",
                    "contig_d256", "paged_b64_t4", "paged_b64_xsplit", "mixed_b256_xsplit"]
 
@@ -107,7 +109,8 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     dev = torch.device("cuda:0")
     pol = {"default": gq.policy_default,
            "pages": gq.policy_pages,
-           "fused": lambda: gq.policy_default(flags=gq.GQA_POLICY_FUSED_MERGE)}[policy_name]()
+           "fused": lambda: gq.policy_default(flags=gq.GQA_POLICY_FUSED_MERGE),
+           "valu": lambda: gq.policy_default(flags=gq.GQA_POLICY_VALU_DOT2)}[policy_name]()
     q = bits_to_device(case.q, case.dtype, dev)
     k0 = bits_to_device(case.k, case.dtype, dev)
     v0 = bits_to_device(case.v, case.dtype, dev)
@@ -339,7 +342,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--policy", default="default", choices=["default", "pages", "fused"])
+    ap.add_argument("--policy", default="default", choices=list(POLICIES))
     ap.add_argument("--no-also", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -390,12 +393,12 @@ def main():
     if not args.no_also:
         for name in BENCH_WORKLOADS:
             c = case if name == args.workload else bench_case(name)
-            for pol in ("default", "pages", "fused"):
+            for pol in POLICIES:
                 if name == args.workload and pol == args.policy:
                     continue
                 if name.endswith(XSPLIT_SUFFIX) and pol != "default":
                     continue
-                if pol == "fused" and name not in FUSED_ROWS:
+                if (pol == "fused" and name not in FUSED_ROWS) or (pol == "valu" and name not in VALU_ROWS):
                     continue
                 r = time_workload(c, pol, args.steps, args.warmup)
                 also[f"{name}/{pol}"] = {k: (round(v, 3) if isinstance(v, float) else v)

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     DecodeArgs,
     GQA_F16,
     GQA_POLICY_FUSED_MERGE,
+    GQA_POLICY_VALU_DOT2,
     GqaError,
     Policy,
     decode,

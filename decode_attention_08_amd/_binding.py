@@ -19,6 +19,7 @@ lib = ctypes.CDLL(library_path)
 GQA_F16 = 0
 GQA_BF16 = 1
 GQA_POLICY_FUSED_MERGE = 1
+GQA_POLICY_VALU_DOT2 = 2
 
 GQA_KV_CONTIGUOUS = 0
 GQA_KV_PAGED = 1
@@ -32,7 +33,7 @@ X = 8   # elements per 16-byte vector of the x-split K layout
 
 class Policy(ctypes.Structure):
     """gqa_policy_t: partition_size, v1_max_ctx, phases (0/3 both, 1 partition, 2 merge),
-    flags (0 or GQA_POLICY_FUSED_MERGE)."""
+    flags (0, GQA_POLICY_FUSED_MERGE or GQA_POLICY_VALU_DOT2)."""
     _fields_ = [("partition_size", ctypes.c_int32), ("v1_max_ctx", ctypes.c_int32),
                 ("phases", ctypes.c_int32), ("flags", ctypes.c_int32)]
 

@@ -54,6 +54,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 32;            // tokens per wave iteration (two 16-token MFMA row blocks)
 constexpr int kMaxHeadsPerGroup = 8; // waves (KV heads) per partition workgroup, at most
@@ -85,6 +87,11 @@ struct F16 {
   static __device__ __forceinline__ float widen(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
   }
+  // c + a.lo * b.lo + a.hi * b.hi in fp32 (v_dot2_f32_f16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                  false);
+  }
 };
 
 struct BF16 {
@@ -97,6 +104,10 @@ struct BF16 {
   }
   static __device__ __forceinline__ float widen(uint32_t bits) {
     return __builtin_bit_cast(float, bits << 16);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
   }
 };
 
@@ -546,6 +557,338 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   }
 }
 
+// ------------------------------------ one wave, one segment, vector ALU --
+//
+// The partial triple of wave_segment with both products on the vector ALU
+// instead of the matrix cores: packed two-element dot products with fp32
+// accumulation (v_dot2_f32_f16 / v_dot2_f32_bf16).  It is there to compare
+// the two units on identical loads (the tile, its lane layout and the
+// non-temporal loads of the row layouts), for d = 128 and NC = 4 or 8
+// columns (G * T_q <= NC; zero query rows pad the rest).
+//   scores   lane (col, grp) holds K rows 16 hb + col, d chunks 4 kk + grp,
+//            and forms partial dot products with every query row (the wave
+//            parks them in LDS; a read is a broadcast to the 16 lanes of a
+//            row).  Two swap-and-add steps across rows (v_permlane16_swap,
+//            v_permlane32_swap) complete them and leave the lane the scores
+//            of token 16 (grp >> 1) + col for columns NH (grp & 1) + h',
+//            h' < NH = NC / 2.
+//   softmax  tile maxima over the 32 lanes of a column set, then exchanged,
+//            so that every lane keeps m of all NC columns; P, as the hi + lo
+//            pair of wave_segment, goes to LDS.
+//   P.V      V is staged in LDS as in wave_segment.  Lane (col, grp) owns
+//            O[h][8 col + e] of the columns h = 4 i + grp, i < NC / 4, over
+//            all tokens: it reads rows 2k and 2k + 1 of d chunk col, repacks
+//            them into token-pair halves, and one dot2 folds both tokens of a
+//            pair into one output element.
+
+constexpr int kDot2D = 128;                       // head dimension of the vector-ALU variant
+
+// LDS per wave, in uint16: the query rows [NC][D], the V tile [32][D], P hi and lo [2][NC][32]
+__host__ __device__ constexpr int dot2_wave_elems(int nc) {
+  return nc * kDot2D + kTile * kDot2D + 2 * nc * kTile;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// Reductions over the 16 lanes of a row; every lane receives the result.
+// quad_perm [1,0,3,2] and [2,3,0,1], then row_half_mirror and row_mirror
+// (after each step the lanes being combined hold equal partial results).
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  return fmaxf(x, dpp<0x140>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  return x + dpp<0x140>(x);
+}
+
+// v_permlane16_swap: the odd 16-lane rows of a trade places with the even
+// rows of b, so a = [a0, b0, a2, b2], b = [a1, b1, a3, b3] afterwards.
+// v_permlane32_swap: the upper 32 lanes of a trade places with the lower 32
+// of b, so a = [a_lo, b_lo], b = [a_hi, b_hi] afterwards.
+// Written as asm with both operands read and written: the compiler's builtins
+// for these instructions (ROCm 7.2) return the first operand's new value as
+// both results.  The two wait states cover a VALU write of an operand just
+// before the swap, as the compiler itself inserts them.
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {
+  __asm__("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_halves32(float& a, float& b) {
+  __asm__("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ float pick4(const float* v, int g) {
+  return g == 0 ? v[0] : g == 1 ? v[1] : g == 2 ? v[2] : v[3];
+}
+
+template <class DT, bool PAGED, int NC>
+__device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt, int s, int j,
+                                                  int t0, int t1, bool complete, float2* pml,
+                                                  int64_t ml_stride, float* po, int64_t o_stride) {
+  constexpr int D = kDot2D;
+  using Gm = Geo<D>;
+  constexpr int KK = Gm::KK, CH = Gm::CH, RPI = Gm::RPI, NIT = Gm::NIT;
+  constexpr int NH = NC / 2;                      // score columns per lane
+  constexpr int NO = NC / 4;                      // output columns per lane
+  static_assert(RPI == 4 && CH == 16 && (NC == 4 || NC == 8), "vector-ALU tile geometry");
+  s = __builtin_amdgcn_readfirstlane(s);
+  j = __builtin_amdgcn_readfirstlane(j);
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const bool odd = grp & 1;
+  const int G = a.group;
+  uint32_t* const qs = reinterpret_cast<uint32_t*>(vt);   // query rows, half pairs [NC][D / 2]
+  uint16_t* const vs = vt + NC * D;                        // V tile [kTile][D]
+  uint16_t* const ps16 = vs + kTile * D;                   // P: hi [NC][kTile], then lo
+  const uint32_t* const ps = reinterpret_cast<const uint32_t*>(ps16);   // token pairs
+
+  // ---- park the query rows in LDS; rows past ncol are zero
+  wave_lds_fence();                               // the previous segment's reads come first
+#pragma unroll
+  for (int i = 0; i < NC / RPI; ++i) {
+    const int h = i * RPI + grp;
+    uint4_t v{0u, 0u, 0u, 0u};
+    if (h < a.ncol) {
+      const int64_t row = ((int64_t)s * a.tq + h / G) * a.h_q + j * G + h % G;
+      v = *reinterpret_cast<const uint4_t*>(a.q + row * D + 8 * col);
+    }
+    *reinterpret_cast<uint4_t*>(qs + h * (D / 2) + 4 * col) = v;
+  }
+  wave_lds_fence();
+
+  float m_run[NC];                                // running max per column, log2 units (all lanes)
+  float l_run[NH];                                // this lane's share of its score columns' sums
+  float acc[NO][8];                               // O[4 i + grp][8 col + e]
+#pragma unroll
+  for (int h = 0; h < NC; ++h) m_run[h] = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) l_run[h] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NO; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+
+  const int64_t trow = (int64_t)s * a.max_blocks;
+  const uint32_t tok_stride = (uint32_t)a.h_kv * D;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+
+  struct Tile {
+    uint4_t k[2][KK];
+    uint4_t v[NIT];
+  };
+  // the row-layout loads of wave_segment: rows past t1 read the last live row
+  auto load = [&](Tile& T, int tb) {
+    const uint16_t* kb[2];
+    const uint16_t* vb[2];
+    int last[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int th = min(tb + 16 * hb, t1 - 1);
+      last[hb] = min(15, t1 - 1 - th);
+      int64_t base;
+      if constexpr (PAGED) {
+        const int32_t blk = load_const(a.block_table, trow + (th >> a.bs_shift));
+        base = ((((int64_t)blk << a.bs_shift) + (th & bs_mask)) * a.h_kv + j) * D;
+      } else {
+        base = (((int64_t)s * a.s_kv + th) * a.h_kv + j) * D;
+      }
+      kb[hb] = a.k + base;
+      vb[hb] = a.v + base;
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + grp;
+      const int hb = r >> 4;
+      const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + 8 * col;
+      T.v[it] = load_stream<uint4_t, true>(vb[hb] + off);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        T.k[hb][kk] = load_stream<uint4_t, true>(kb[hb] + roff + 8 * (kk * 4 + grp));
+    }
+  };
+
+  const int tt = 16 * (grp >> 1) + col;           // the lane's token within a tile (scores)
+
+  auto compute = [&](const Tile& T, int tb) {
+    // stage V: row 4 it + grp, d chunk col
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      *reinterpret_cast<uint4_t*>(vs + (it * RPI + grp) * D + 8 * col) = T.v[it];
+    // ---- scores: partial sums over the lane's d chunks, then across the four rows
+    float sc[2][NC];
+#pragma unroll
+    for (int h = 0; h < NC; ++h) sc[0][h] = sc[1][h] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int h = 0; h < NC; ++h) {
+        const uint4_t qv = *reinterpret_cast<const uint4_t*>(qs + h * (D / 2) + (4 * kk + grp) * 4);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[hb][h] = DT::dot2(T.k[hb][kk][e], qv[e], sc[hb][h]);
+      }
+    float x[NH];
+    float alpha[NC];
+    {
+      float m_tile[NC];
+      const bool live = tb + tt < t1;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        float a0 = sc[0][h], b0 = sc[0][h + NH], a1 = sc[1][h], b1 = sc[1][h + NH];
+        swap_rows16(a0, b0);
+        swap_rows16(a1, b1);
+        float x0 = a0 + b0, x1 = a1 + b1;         // even rows: column h; odd rows: h + NH
+        swap_halves32(x0, x1);
+        x[h] = live ? (x0 + x1) * a.c : -INFINITY;
+        float mx = row_max16(x[h]);
+        float my = mx;
+        swap_halves32(mx, my);
+        mx = fmaxf(mx, my);                       // tile max of the lane's column
+        float ma = mx, mb = mx;
+        swap_rows16(ma, mb);                      // ma: column h, mb: column h + NH
+        m_tile[h] = ma;
+        m_tile[h + NH] = mb;
+      }
+#pragma unroll
+      for (int h = 0; h < NC; ++h) {
+        const float m_new = fmaxf(m_run[h], m_tile[h]);   // finite: the tile holds a live token
+        alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+        m_run[h] = m_new;
+      }
+    }
+    // ---- P (hi + lo pair in the storage dtype) to LDS
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float mh = odd ? m_run[h + NH] : m_run[h];
+      const float ah = odd ? alpha[h + NH] : alpha[h];
+      const float p = __builtin_amdgcn_exp2f(x[h] - mh);
+      l_run[h] = l_run[h] * ah + p;
+      const uint32_t hi = DT::narrow(p);
+      const uint32_t lo = DT::narrow(p - DT::widen(hi));
+      uint16_t* dst = ps16 + (h + (odd ? NH : 0)) * kTile + tt;
+      dst[0] = (uint16_t)hi;
+      dst[NC * kTile] = (uint16_t)lo;
+    }
+    wave_lds_fence();
+    // ---- O += P . V over token pairs (2k, 2k + 1), d = 8 col + e, columns 4 i + grp
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const float al = pick4(alpha + 4 * i, grp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] *= al;
+    }
+    // (a rolled loop: unrolled, the LDS reads of all 16 pairs are hoisted and spill)
+#pragma nounroll
+    for (int q4 = 0; q4 < kTile / 8; ++q4) {      // pairs 4 q4 .. 4 q4 + 3
+      uint4_t ph[NO], pl[NO];
+#pragma unroll
+      for (int i = 0; i < NO; ++i) {
+        const int h = 4 * i + grp;
+        ph[i] = *reinterpret_cast<const uint4_t*>(ps + h * (kTile / 2) + 4 * q4);
+        pl[i] = *reinterpret_cast<const uint4_t*>(ps + (NC + h) * (kTile / 2) + 4 * q4);
+      }
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        const int t = 8 * q4 + 2 * kp;
+        const uint4_t r0 = *reinterpret_cast<const uint4_t*>(vs + t * D + 8 * col);
+        const uint4_t r1 = *reinterpret_cast<const uint4_t*>(vs + (t + 1) * D + 8 * col);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t v_lo = __builtin_amdgcn_perm(r1[e2], r0[e2], 0x05040100u);  // d = 8 col + 2 e2
+          const uint32_t v_hi = __builtin_amdgcn_perm(r1[e2], r0[e2], 0x07060302u);  // d + 1
+#pragma unroll
+          for (int i = 0; i < NO; ++i) {
+            acc[i][2 * e2] = DT::dot2(v_lo, ph[i][kp], acc[i][2 * e2]);
+            acc[i][2 * e2] = DT::dot2(v_lo, pl[i][kp], acc[i][2 * e2]);
+            acc[i][2 * e2 + 1] = DT::dot2(v_hi, ph[i][kp], acc[i][2 * e2 + 1]);
+            acc[i][2 * e2 + 1] = DT::dot2(v_hi, pl[i][kp], acc[i][2 * e2 + 1]);
+          }
+        }
+      }
+    }
+    wave_lds_fence();                             // reads retire before the next tile's stores
+  };
+
+  // ---- token loop: the two-tile ping-pong of wave_segment
+  int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
+  if (n > 0) {
+    Tile A, B;
+    int tb = t0;
+    load(A, tb);
+    while (n >= 3) {
+      load(B, tb + kTile);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, tb);
+      load(A, tb + 2 * kTile);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B, tb + kTile);
+      tb += 2 * kTile;
+      n -= 2;
+    }
+    if (n == 2) {
+      load(B, tb + kTile);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, tb);
+      compute(B, tb + kTile);
+    } else {
+      compute(A, tb);
+    }
+  }
+
+  // ---- epilogue: l of every column (its 32 lanes hold the shares)
+  float l_all[NC];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float l = row_sum16(l_run[h]);
+    float l2 = l;
+    swap_halves32(l, l2);
+    l += l2;
+    float la = l, lb = l;
+    swap_rows16(la, lb);
+    l_all[h] = la;
+    l_all[h + NH] = lb;
+  }
+  const float (&o)[NO][8] = acc;
+  const bool seg_empty = t1 <= t0;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    const int h = 4 * i + grp;
+    if (h >= a.ncol) continue;
+    const float lh = pick4(l_all + 4 * i, grp);
+    if (complete) {
+      const int64_t row = ((int64_t)s * a.tq + h / G) * a.h_q + j * G + h % G;
+      uint4_t w{0u, 0u, 0u, 0u};
+      if (!seg_empty) {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          w[e2] = DT::narrow(o[i][2 * e2] / lh) | (DT::narrow(o[i][2 * e2 + 1] / lh) << 16);
+      }
+      *reinterpret_cast<uint4_t*>(a.out + row * D + 8 * col) = w;
+    } else {
+      float4_t* dst = reinterpret_cast<float4_t*>(po + (int64_t)h * o_stride + 8 * col);
+      dst[0] = float4_t{o[i][0], o[i][1], o[i][2], o[i][3]};
+      dst[1] = float4_t{o[i][4], o[i][5], o[i][6], o[i][7]};
+      if (col == 0) pml[(int64_t)h * ml_stride] = make_float2(pick4(m_run + 4 * i, grp), lh);
+    }
+  }
+}
+
 // ------------------------------------------------- fixed-partition kernel --
 //
 // One workgroup per (partition p, head group, sequence s), one wave per KV
@@ -666,8 +1009,10 @@ __device__ __forceinline__ int64_t range_prefix(const Params& a, const int32_t* 
     return (int64_t)s * a.n_groups * seq_tiles(a.s_kv);
 }
 
-template <class DT, int D, bool PAGED, bool XS, bool SPLIT, bool FUSED>
+// VC > 0 selects the vector-ALU segment code with VC columns (wave_segment_dot2).
+template <class DT, int D, bool PAGED, bool XS, bool SPLIT, bool FUSED, int VC = 0>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balanced_kernel(Params a) {
+  static_assert(VC == 0 || (D == kDot2D && !XS && !SPLIT && !FUSED), "vector-ALU variant shape");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // wave tiles, then the prefix
   __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
   __shared__ float2 mlx[kMaxHeadsPerGroup * 16];                     // sub-wave (m, l) exchange
@@ -677,7 +1022,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   const int nw = blockDim.x >> 6;                // = hpw * wph
   // per-wave tiles: V staging (row layout) and the sub-wave state exchange;
   // the x-split layout with one wave per head needs neither
-  constexpr int tile_elems = (XS && !SPLIT) ? 0 : Geo<D>::V_TILE;
+  constexpr int tile_elems = VC > 0 ? dot2_wave_elems(VC) : (XS && !SPLIT) ? 0 : Geo<D>::V_TILE;
   uint16_t* const vt = smem + w * tile_elems;
   int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * tile_elems);
 
@@ -756,9 +1101,13 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
     }
     if (run) {
       const int64_t hrow = (int64_t)slot * heads + (SPLIT ? w % a.hpw : w) * a.ncol;
-      wave_segment<DT, D, PAGED, XS, true, SPLIT>(
-          a, smem, vt, mlx, s, j, t0, t1, complete, complete ? nullptr : a.part_ml + hrow, 1,
-          complete ? nullptr : a.part_o + hrow * D, D);
+      float2* const pml = complete ? nullptr : a.part_ml + hrow;
+      float* const po = complete ? nullptr : a.part_o + hrow * D;
+      if constexpr (VC > 0)
+        wave_segment_dot2<DT, PAGED, VC>(a, vt, s, j, t0, t1, complete, pml, 1, po, D);
+      else
+        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, complete, pml,
+                                                    1, po, D);
       if (threadIdx.x == 0) {
         if (complete) {
           if (a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
@@ -997,8 +1346,9 @@ gqa_status_t resolve_policy(const gqa_policy_t* in, gqa_policy_t* out) {
   if ((!balanced && (out->partition_size < kTile || out->partition_size > (1 << 20) ||
                      out->partition_size % kTile != 0)) ||
       out->v1_max_ctx < 0 || out->phases < 0 || out->phases > 3 ||
-      (out->flags & ~GQA_POLICY_FUSED_MERGE) != 0 ||
-      ((out->flags & GQA_POLICY_FUSED_MERGE) && !balanced))
+      (out->flags & ~(GQA_POLICY_FUSED_MERGE | GQA_POLICY_VALU_DOT2)) != 0 ||
+      ((out->flags & (GQA_POLICY_FUSED_MERGE | GQA_POLICY_VALU_DOT2)) && !balanced) ||
+      ((out->flags & GQA_POLICY_FUSED_MERGE) && (out->flags & GQA_POLICY_VALU_DOT2)))
     return GQA_ERR_BAD_POLICY;
   if (out->phases == 0) out->phases = 3;
   return GQA_OK;
@@ -1023,6 +1373,7 @@ struct Plan {
   int max_parts;      // fixed mode
   bool can_split;     // some sequence may exceed v1_max_ctx
   bool fused;         // split ranges merged by their last workgroup (no merge kernel)
+  int vc;             // vector-ALU products with vc columns (4 or 8); 0: matrix cores
   size_t ws_desc, ws_cnt, ws_ml, ws_o, ws_total;   // byte sizes of the workspace regions
 };
 
@@ -1046,8 +1397,10 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
   // which split each segment's tiles: a lone wave per head walking a short
   // sequence is latency-bound.  Larger groups have waves enough; on a batch of
   // 256 sequences of ~3400 tokens with four KV heads the split cost 2%.
-  if (pl.balanced && pl.hpw <= 2 && !(pol.flags & GQA_POLICY_FUSED_MERGE))
+  if (pl.balanced && pl.hpw <= 2 && !(pol.flags & (GQA_POLICY_FUSED_MERGE | GQA_POLICY_VALU_DOT2)))
     pl.wph = max_heads_per_group(d) / pl.hpw;
+  if (pl.balanced && (pol.flags & GQA_POLICY_VALU_DOT2))
+    pl.vc = (h_q / h_kv) * t_q <= 4 ? 4 : 8;
   pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
   if (!pl.can_split) return pl;
@@ -1100,11 +1453,18 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds, int* cus_out = 
 // Per-wave LDS tiles: V staging (row layout) and the sub-wave state exchange.
 template <int D, bool XS>
 size_t tiles_lds(const Plan& pl) {
+  if (pl.vc > 0) return (size_t)pl.hpw * dot2_wave_elems(pl.vc) * sizeof(uint16_t);
   return (XS && pl.wph == 1) ? 0 : (size_t)pl.hpw * pl.wph * Geo<D>::V_TILE * sizeof(uint16_t);
 }
 
 template <class DT, int D, bool PAGED, bool XS>
 const void* balanced_kernel(const Plan& pl) {
+  if constexpr (D == kDot2D && !XS) {
+    if (pl.vc == 4)
+      return reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false, false, 4>);
+    if (pl.vc == 8)
+      return reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false, false, 8>);
+  }
   if (pl.fused)   // one wave per head (make_plan)
     return reinterpret_cast<const void*>(&partition_balanced_kernel<DT, D, PAGED, XS, false, true>);
   return pl.wph > 1
@@ -1258,7 +1618,10 @@ gqa_status_t run(const Problem& pb) {
   const int64_t max_ctx64 = pb.paged ? (int64_t)pb.max_blocks * pb.block_size : pb.s_kv;
   if (max_ctx64 > (1 << 30)) return GQA_ERR_BAD_SHAPE;
   const int max_ctx = (int)max_ctx64;
+  if ((pol.flags & GQA_POLICY_VALU_DOT2) && (pb.d != kDot2D || pb.xsplit || G * pb.tq > 8))
+    return GQA_ERR_UNSUPPORTED;
   const Plan pl = make_plan(pb.num_seqs, pb.tq, pb.h_q, pb.h_kv, pb.d, max_ctx, pol);
+  if ((pol.flags & GQA_POLICY_VALU_DOT2) && !pl.balanced) return GQA_ERR_UNSUPPORTED;
   if (!pl.balanced && (int64_t)pl.max_parts * pl.n_groups * pb.num_seqs > INT32_MAX)
     return GQA_ERR_BAD_SHAPE;
   if ((int64_t)pb.h_q * pb.tq * pb.num_seqs > INT32_MAX) return GQA_ERR_BAD_SHAPE;

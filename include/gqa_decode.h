@@ -104,8 +104,10 @@ typedef enum gqa_status {
  * The balanced decomposition needs num_seqs <= 8192; a larger batch uses the
  * fixed one with 512-token partitions.
  *
- * flags: 0, or GQA_POLICY_FUSED_MERGE (balanced decomposition only; other
- * bits are errors).  With it, the workgroup that finishes a split range last
+ * flags: 0, GQA_POLICY_FUSED_MERGE or GQA_POLICY_VALU_DOT2 (each for the
+ * balanced decomposition only, and not both; other bits are errors).
+ *
+ * GQA_POLICY_FUSED_MERGE: the workgroup that finishes a split range last
  * merges that range itself (it finds out through a per-range atomic counter in
  * the workspace; nothing waits on anything), and no merge kernel is launched.
  * It saves the merge launch, but a range's merge then runs on one CU, so it
@@ -113,14 +115,24 @@ typedef enum gqa_status {
  * must be zero-filled before its first call with this flag (for instance when
  * it is allocated); every call that runs to completion leaves the counters at
  * zero again, graph replays included.  phases 2 then does nothing.
+ *
+ * GQA_POLICY_VALU_DOT2: the partition kernel computes Q.K^T and P.V on the
+ * vector ALU, as packed two-element dot products with fp32 accumulation
+ * (v_dot2_f32_f16 / v_dot2_f32_bf16), instead of on the matrix cores; loads,
+ * decomposition, partials and merge are unchanged.  It exists to compare the
+ * two units.  Supported for d_head = 128, the contiguous and row-layout paged
+ * caches and G * T_q <= 8 with the balanced decomposition; any other problem
+ * returns GQA_ERR_UNSUPPORTED.  Groups of one or two KV heads get one wave
+ * per head (no split of segments between waves).
  */
 #define GQA_POLICY_FUSED_MERGE 1
+#define GQA_POLICY_VALU_DOT2 2
 
 typedef struct gqa_policy {
   int32_t partition_size;
   int32_t v1_max_ctx;
   int32_t phases;
-  int32_t flags;           /* 0 or GQA_POLICY_FUSED_MERGE */
+  int32_t flags;           /* 0, GQA_POLICY_FUSED_MERGE or GQA_POLICY_VALU_DOT2 */
 } gqa_policy_t;
 
 /* Fill *p with the MI355X default policy. */

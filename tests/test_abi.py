@@ -131,7 +131,8 @@ def test_policy_and_workspace_errors(gq):
     for pol in (gq.Policy(100, 0, 0, 0), gq.Policy(16, 0, 0, 0), gq.Policy(-32, 0, 0, 0),
                 gq.Policy(512, -1, 0, 0), gq.Policy(0, -1, 0, 0), gq.Policy(512, 0, 4, 0),
                 gq.Policy(0, 0, -1, 0), gq.Policy(512, 0, 0, 1), gq.Policy(1 << 21, 0, 0, 0),
-                gq.Policy(0, 0, 0, 2), gq.Policy(0, 0, 0, -1)):
+                gq.Policy(0, 0, 0, 4), gq.Policy(0, 0, 0, -1), gq.Policy(0, 0, 0, 3),
+                gq.Policy(512, 0, 0, 2)):
         assert _call(gq, policy=pol) == ERR["POLICY"], pol
         assert _call(gq, "gqa_decode_xsplit", policy=pol) == ERR["POLICY"], pol
     for pol in (gq.policy_pages(v1_max_ctx=0), gq.policy_default(v1_max_ctx=0)):
@@ -220,3 +221,22 @@ def test_fused_policy_workspace(gq):
     assert fused == plain + 256                                  # 3 counters, 256-aligned
     assert gq.workspace_size(3, 32, 8, 128, 200, F) == 0         # nothing can split
     assert gq.workspace_size(3, 32, 8, 128, 4096, gq.Policy(512, 8192, 0, 1)) == 0   # fixed: invalid
+
+
+def test_valu_policy_support(gq):
+    """GQA_POLICY_VALU_DOT2 is for d = 128, row layouts and G * T_q <= 8; the
+    workspace is that of the balanced decomposition."""
+    V = gq.policy_default(flags=gq.GQA_POLICY_VALU_DOT2)
+    assert gq.workspace_size(3, 32, 8, 128, 4096, V) == \
+        gq.workspace_size(3, 32, 8, 128, 4096, gq.policy_default())
+    assert _call(gq, policy=V, d=64) == ERR["UNSUP"]
+    assert _call(gq, policy=V, d=256) == ERR["UNSUP"]
+    assert _call(gq, policy=V, h_q=32, h_kv=2) == ERR["UNSUP"]          # G = 16
+    assert _call(gq, "gqa_decode_xsplit", policy=V) == ERR["UNSUP"]
+    assert gq.lib.gqa_decode_ex(ctypes.byref(_ex(gq, t_q=3, policy=ctypes.pointer(V)))) == \
+        ERR["UNSUP"]                                                    # G * T_q = 12
+    # supported shapes pass every check and fail only on the bad workspace pointer
+    assert _call(gq, policy=V, ws=A + 16, max_blocks=512) == ERR["ALIGN"]
+    assert gq.lib.gqa_decode_ex(ctypes.byref(
+        _ex(gq, t_q=2, max_blocks_per_seq=512, workspace=A + 16,
+            policy=ctypes.pointer(V)))) == ERR["ALIGN"]
