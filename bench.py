@@ -11,9 +11,11 @@ Prints ONE JSON line.  `value` is K+V GB/s of the headline workload
 (algorithmic K+V bytes / wall time per step between synchronisations);
 `roofline` gives the partition kernel's own HBM roofline fraction, its mean
 launch duration timed with HIP events on the launch stream around the timed
-steps' partition launches issued back to back; `cpu_baseline` times
-the float64 oracle on a bounded sample of the same workload; `also` carries
-the other full-size workloads.
+steps' partition launches issued back to back, and its fraction of the
+achievable read rate a streaming-read probe measures (`read_probe`, context
+beside the published peak); `cpu_baseline` times the float64 oracle on a
+bounded sample of the same workload, in a pool of worker processes; `also`
+carries the other full-size workloads.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload contig_b8]
   python bench.py --summarize-rocprof DIR     # rocprofv3 csv -> short text
@@ -38,6 +40,9 @@ ROTATE_BYTES = 1 << 30                  # K/V bytes cycled per step sequence
 HEADLINE = "contig_b8"
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_08_amd", "csrc", "gqa_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROBE_LIB = os.path.join(ROOT, "decode_attention_08_amd", "libhbm_probe.so")
+PROBE_BYTES = 4 << 30                   # streaming-read probe buffer
+CPU_WORKERS_MAX = 16                    # oracle pool: at most the host's share for one GPU
 
 
 def source_hash() -> str:
@@ -206,35 +211,108 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     return res
 
 
-def cpu_baseline(case, budget_s: float = 10.0):
-    """The float64 oracle, as it stands, over whole (sequence, KV head) slices of the
-    workload in a seeded order, one BLAS thread, repeating passes until about
-    budget_s of CPU time."""
-    from threadpoolctl import threadpool_limits
+def _cpu_worker(name: str, w: int, n: int, budget_s: float, barrier, results):
+    """One oracle worker: rebuilds the seeded workload, waits for the others,
+    then walks its share of the (sequence, KV head) slices (every n-th of a
+    seeded order, repeated) for budget_s of wall time with one BLAS thread."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     from oracle import reference as R
 
+    case = bench_case(name)
     G = case.h_q // case.h_kv
     pairs = [(s, j) for s in range(case.num_seqs) for j in range(case.h_kv)]
     order = np.random.default_rng(0).permutation(len(pairs))
-    done_bytes, done_pairs, t_used = 0, 0, 0.0
+    mine = [pairs[i] for i in order[w::n]] or [pairs[order[w % len(pairs)]]]
+    done_bytes, done_pairs = 0, 0
     with threadpool_limits(limits=1):
-        while t_used < budget_s:
-            for n in order:
-                s, j = pairs[n]
-                heads = [(s, j * G + g) for g in range(G)]
-                t0 = time.perf_counter()
-                R.decode(case, heads=heads)
-                t_used += time.perf_counter() - t0
-                done_bytes += int(case.ctx_lens[s]) * case.d * 2 * 2
-                done_pairs += 1
-                if t_used >= budget_s:
-                    break
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{done_pairs} (sequence, KV head) slices of {case.name} "
-                       f"({len(pairs)} per step, repeated in a seeded order), {done_bytes} K/V "
-                       f"bytes in {t_used:.2f} s; float64 numpy oracle, 1 BLAS thread"),
+        barrier.wait()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            s, j = mine[done_pairs % len(mine)]
+            R.decode(case, heads=[(s, j * G + g) for g in range(G)])
+            done_bytes += int(case.ctx_lens[s]) * case.d * 2 * 2
+            done_pairs += 1
+        elapsed = time.perf_counter() - t0
+    results.put((done_bytes, done_pairs, elapsed))
+
+
+def cpu_baseline(name: str, budget_s: float = 10.0):
+    """The float64 oracle, as it stands, on the workload `name`: a pool of
+    worker processes (one per available core, at most CPU_WORKERS_MAX), each
+    with one BLAS thread, over whole (sequence, KV head) slices for about
+    budget_s of wall time.  Rate = all workers' K/V bytes / the longest
+    worker's time.  The workers are started fresh (spawn) and must be started
+    before this process uses the GPU."""
+    import multiprocessing as mp
+
+    n = max(1, min(CPU_WORKERS_MAX, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(n)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker, args=(name, w, n, budget_s, barrier, results))
+             for w in range(n)]
+    for p in procs:
+        p.start()
+    got = [results.get(timeout=600) for _ in procs]
+    for p in procs:
+        p.join(timeout=60)
+    done_bytes = sum(g[0] for g in got)
+    done_pairs = sum(g[1] for g in got)
+    t_used = max(g[2] for g in got)
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": (f"{done_pairs} (sequence, KV head) slices of {name} over {n} worker "
+                       f"processes (each every {n}-th slice of a seeded order, repeated), "
+                       f"{done_bytes} K/V bytes in {t_used:.2f} s; float64 numpy oracle, one "
+                       f"BLAS thread per worker"),
             "seconds": round(t_used, 3)}
+
+
+def read_probe(reps: int = 10):
+    """Achievable HBM read rate: the streaming-read probe (libhbm_probe.so)
+    reading a PROBE_BYTES buffer, `reps` launches back to back between HIP
+    events on the launch stream; best over its two access patterns and three
+    grid sizes."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32,
+                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    buf = torch.full((PROBE_BYTES,), 0x5A, dtype=torch.uint8, device=dev)   # folds to 0
+    key = 0xFFFFFFFF                                                       # never matched
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.Stream(device=dev)
+    sink = torch.zeros(cus * 8 * 256, dtype=torch.int32, device=dev)
+    best = (0.0, 0, 0)
+    sweep = {}
+    for mode in (0, 1):
+        for per_cu in (2, 4, 8):
+            grid = cus * per_cu
+            args = (buf.data_ptr(), PROBE_BYTES, key, sink.data_ptr(), grid, mode,
+                    ctypes.c_void_p(stream.cuda_stream))
+            torch.cuda.synchronize()
+            for _ in range(2):
+                assert lib.hbm_read_probe(*args) == 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                assert lib.hbm_read_probe(*args) == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            gbs = PROBE_BYTES * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+            sweep[f"{('stride', 'chunked')[mode]}/{per_cu}_per_cu"] = round(gbs, 1)
+            if gbs > best[0]:
+                best = (gbs, grid, mode)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"gbs": round(best[0], 1), "bytes": PROBE_BYTES, "grid": best[1],
+            "pattern": ("grid-stride", "chunked")[best[2]],
+            "pct_of_peak": round(100.0 * best[0] / PEAK_GBS, 2), "sweep": sweep,
+            "method": "16-byte non-temporal loads, 8 in flight per lane, 256-lane workgroups; "
+                      "mean over back-to-back launches between HIP events"}
 
 
 def _round(x, nd: int = 2):
@@ -371,8 +449,10 @@ def main():
               "sharding across GPUs is not built.", file=sys.stderr)
         return 2
 
+    # the oracle pool first: its workers start before this process touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline(args.workload)
+
     import torch
-    import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     case = bench_case(args.workload)
@@ -407,7 +487,7 @@ def main():
                       f"partition {r['partition_us_mean']:.1f} us ({r['partition_gbs']:.0f} GB/s)",
                       file=sys.stderr, flush=True)
 
-    cpu = None if args.no_cpu else cpu_baseline(case)
+    probe = None if args.no_also else read_probe()
     achieved = head["partition_gbs"]
     traffic, rocprof_us = traffic_for(case.name, args.policy)
     line = {
@@ -443,7 +523,9 @@ def main():
                      "kernel_us_rocprof": rocprof_us,
                      "valu_busy_pct": _round(traffic_record(case.name, args.policy).get("valu_busy_pct")),
                      "mfma_util_pct": _round(traffic_record(case.name, args.policy).get("mfma_util_pct")),
-                     "merge_us_mean": round(head["merge_us_mean"], 3)},
+                     "merge_us_mean": round(head["merge_us_mean"], 3),
+                     "frac_of_read_probe": (round(achieved / probe["gbs"], 4) if probe else None)},
+        "read_probe": probe,
         "cpu_baseline": cpu,
         "also": also,
         "kernel_source_sha": source_hash(),

@@ -43,3 +43,30 @@ def test_traffic_record_requires_matching_source(tmp_path, monkeypatch):
 def test_bench_workloads_build_names():
     assert "contig_b8" in bench.BENCH_WORKLOADS
     assert bench.bench_desc("paged_b64_xsplit").endswith("x-split pool layout")
+
+
+def test_cpu_baseline_pool_reports_its_workers():
+    import bench
+    rec = bench.cpu_baseline("tiny_contig", budget_s=0.3)
+    assert rec["kind"] == "oracle" and rec["unit"] == "GB/s"
+    assert 1 <= rec["cores"] <= bench.CPU_WORKERS_MAX
+    assert rec["value"] > 0 and rec["seconds"] >= 0.3
+    assert f"over {rec['cores']} worker processes" in rec["sample"]
+
+
+def test_read_probe_library_validates_arguments():
+    """The probe library loads and rejects bad arguments before any HIP call."""
+    import ctypes
+    import bench
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    f = lib.hbm_read_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    for mode in (0, 1):
+        assert f(None, 1 << 20, 0, 0x10000, 64, mode, None) == 1      # no buffer
+        assert f(0x10000, 1 << 20, 0, None, 64, mode, None) == 1      # no sink
+        assert f(0x10000, 1 << 20, 0, 0x20000, 0, mode, None) == 1    # empty grid
+        assert f(0x10000, 1000, 0, 0x20000, 64, mode, None) == 1      # not a multiple of 16
+        assert f(0x10008, 1 << 20, 0, 0x20000, 64, mode, None) == 1   # misaligned
+    assert f(0x10000, 1 << 20, 0, 0x20000, 64, 2, None) == 1          # unknown pattern
