@@ -271,8 +271,8 @@ def cpu_baseline(name: str, budget_s: float = 10.0):
 def read_probe(reps: int = 10):
     """Achievable HBM read rate: the streaming-read probe (libhbm_probe.so)
     reading a PROBE_BYTES buffer, `reps` launches back to back between HIP
-    events on the launch stream; best over its two access patterns and three
-    grid sizes."""
+    events on the launch stream; best over its access patterns (grid-stride;
+    chunked with 8, 16 or 32 loads in flight per lane) and grid sizes."""
     import ctypes
     import torch
 
@@ -288,8 +288,9 @@ def read_probe(reps: int = 10):
     sink = torch.zeros(cus * 8 * 256, dtype=torch.int32, device=dev)
     best = (0.0, 0, 0)
     sweep = {}
-    for mode in (0, 1):
-        for per_cu in (2, 4, 8):
+    names = ("stride8", "chunked8", "chunked16", "chunked32")
+    for mode in range(4):
+        for per_cu in ((2, 4, 8) if mode == 0 else (1, 2, 4, 8)):
             grid = cus * per_cu
             args = (buf.data_ptr(), PROBE_BYTES, key, sink.data_ptr(), grid, mode,
                     ctypes.c_void_p(stream.cuda_stream))
@@ -303,15 +304,15 @@ def read_probe(reps: int = 10):
             b.record(stream)
             torch.cuda.synchronize()
             gbs = PROBE_BYTES * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-            sweep[f"{('stride', 'chunked')[mode]}/{per_cu}_per_cu"] = round(gbs, 1)
+            sweep[f"{names[mode]}/{per_cu}_per_cu"] = round(gbs, 1)
             if gbs > best[0]:
                 best = (gbs, grid, mode)
     del buf, sink
     torch.cuda.empty_cache()
     return {"gbs": round(best[0], 1), "bytes": PROBE_BYTES, "grid": best[1],
-            "pattern": ("grid-stride", "chunked")[best[2]],
+            "pattern": names[best[2]],
             "pct_of_peak": round(100.0 * best[0] / PEAK_GBS, 2), "sweep": sweep,
-            "method": "16-byte non-temporal loads, 8 in flight per lane, 256-lane workgroups; "
+            "method": "16-byte non-temporal loads, 256-lane workgroups; "
                       "mean over back-to-back launches between HIP events"}
 
 

@@ -63,10 +63,11 @@ def test_read_probe_library_validates_arguments():
     f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p,
                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     f.restype = ctypes.c_int
-    for mode in (0, 1):
+    for mode in (0, 1, 2, 3):
         assert f(None, 1 << 20, 0, 0x10000, 64, mode, None) == 1      # no buffer
         assert f(0x10000, 1 << 20, 0, None, 64, mode, None) == 1      # no sink
         assert f(0x10000, 1 << 20, 0, 0x20000, 0, mode, None) == 1    # empty grid
         assert f(0x10000, 1000, 0, 0x20000, 64, mode, None) == 1      # not a multiple of 16
         assert f(0x10008, 1 << 20, 0, 0x20000, 64, mode, None) == 1   # misaligned
-    assert f(0x10000, 1 << 20, 0, 0x20000, 64, 2, None) == 1          # unknown pattern
+    assert f(0x10000, 1 << 20, 0, 0x20000, 64, 4, None) == 1          # unknown pattern
+    assert f(0x10000, 1 << 20, 0, 0x20000, 64, -1, None) == 1         # unknown pattern
