@@ -122,7 +122,7 @@ struct Params {
   const int32_t* ctx_lens;      // paged only
   float2* part_ml;              // partial (m in log2 units, l) per (slot, query head)
   float* part_o;                // partial un-normalised O row per (slot, query head)
-  int4* desc;                   // balanced mode: per (sequence, head group) segment record
+  int4* desc;                   // balanced mode, paged: per (sequence, head group) segment record
   int* cnt;                     // fused merge: segments finished per (sequence, head group)
   int num_seqs;
   int h_q;
@@ -140,6 +140,9 @@ struct Params {
   int part_size;                // fixed mode: tokens per partition
   int v1_max_ctx;               // sequences this short are never split
   int max_parts;                // fixed mode: partition slots per (sequence, query head)
+  int pchunk;                   // balanced mode, contiguous: tiles per workgroup share,
+  uint32_t pchunk_m;            //   and n / pchunk = (n * pchunk_m) >> pchunk_s for n < 2^30
+  int pchunk_s;
   float c;                      // scale * log2(e)
 };
 
@@ -996,7 +999,8 @@ __device__ __forceinline__ void fused_range_merge(const Params& a, int s, int hg
 // segments of a split range write fp32 partials to per-workgroup slots
 // (2w for the range the share starts in, 2w + 1 for the one it ends in) and
 // the range's first segment records (first workgroup, last workgroup, first
-// slot) for the merge kernel.
+// slot) for the merge kernel; with a contiguous cache every range has the same
+// length, and the merge kernel computes the record instead.
 
 // The prefix lives in LDS, which the compiler treats as per-lane data; every
 // lane reads the same entry, so readfirstlane keeps the scheduling arithmetic
@@ -1108,7 +1112,8 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
       else
         wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, complete, pml,
                                                     1, po, D);
-      if (threadIdx.x == 0) {
+      // (a contiguous cache's records are arithmetic: the merge recomputes them)
+      if (PAGED && threadIdx.x == 0) {
         if (complete) {
           if (a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
         } else if (t0 == 0) {
@@ -1174,6 +1179,23 @@ __host__ __device__ constexpr int merge_heads_per_block(int spi) {
   return merge_block(spi) / (kMergeLanes * spi);
 }
 
+// The record the balanced partition kernel would write for range r of a
+// contiguous cache, computed instead of loaded (a load would be the merge's
+// first dependent memory access): every range holds seq_tiles(s_kv) tiles and
+// the host passes the share size.  Returns (first workgroup, last workgroup,
+// first slot); a range written in one pass has first == last.  The balanced
+// plan keeps the tile count below 2^30, and the divisions by the share size
+// are a multiply and a shift with the host's constants (exact below 2^30).
+__device__ __forceinline__ int4 contiguous_record(const Params& a, int r) {
+  const uint32_t nt = (uint32_t)seq_tiles(a.s_kv);
+  const uint32_t chunk = (uint32_t)a.pchunk;
+  const uint32_t rs = (uint32_t)r * nt;
+  const int wg0 = (int)(((uint64_t)rs * a.pchunk_m) >> a.pchunk_s);
+  const int wg1 = (int)(((uint64_t)(rs + nt - 1) * a.pchunk_m) >> a.pchunk_s);
+  if (a.s_kv <= a.v1_max_ctx || wg0 == wg1) return make_int4(wg0, wg0, -1, 0);
+  return make_int4(wg0, wg1, 2 * wg0 + (rs == (uint32_t)wg0 * chunk ? 0 : 1), 0);
+}
+
 // SLICED: a head's d is cut into D / 32 slices of 32, each merged by its own
 // slots (every slice reads all partials' (m, l), and its 128 bytes of each O
 // row).  It multiplies the workgroups of a merge with few heads and many
@@ -1212,7 +1234,10 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
     const int j = i / a.group;                    // KV head
     const int c = tau * a.group + i % a.group;    // column of KV head j's partial rows
     if constexpr (BALANCED) {
-      d = a.desc[s * a.n_groups + j / a.hpw];
+      if constexpr (PAGED)
+        d = a.desc[s * a.n_groups + j / a.hpw];
+      else
+        d = contiguous_record(a, s * a.n_groups + j / a.hpw);
       n = d.y == d.x ? 0 : d.y - d.x + 1;
       local = (j % a.hpw) * a.ncol + c;
     } else {
@@ -1517,12 +1542,28 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
   Params local = prm;
   void* args[] = {&local};
   const int block = 64 * pl.hpw * pl.wph;
+  int grid_b = 0;                                 // balanced partition grid
+  if (pl.balanced) {
+    grid_b = balanced_grid<DT, D, PAGED, XS>(prm, pl);
+    if (grid_b <= 0) return GQA_ERR_LAUNCH;
+    if (!PAGED) {
+      // the share size the partition kernel derives, for the merge kernel
+      const int64_t total = (int64_t)prm.num_seqs * pl.n_groups *
+                            std::max<int64_t>(1, ((int64_t)prm.s_kv + kTile - 1) / kTile);
+      const int64_t chunk = std::max<int64_t>((total + grid_b - 1) / grid_b, kMinChunkTiles);
+      // division by chunk for numerators below 2^30: shift s = 30 + ceil(log2 chunk) and
+      // multiplier ceil(2^s / chunk) < 2^32 (the round-up method of Granlund and Montgomery)
+      int l = 0;
+      while ((int64_t(1) << l) < chunk) ++l;
+      local.pchunk = (int)chunk;
+      local.pchunk_s = 30 + l;
+      local.pchunk_m = (uint32_t)(((uint64_t(1) << (30 + l)) + chunk - 1) / chunk);
+    }
+  }
   if (phases & 1) {
     if (pl.balanced) {
       const void* kern = balanced_kernel<DT, D, PAGED, XS>(pl);
-      const int grid = balanced_grid<DT, D, PAGED, XS>(prm, pl);
-      if (grid <= 0) return GQA_ERR_LAUNCH;
-      if (hipLaunchKernel(kern, dim3(grid), dim3(block), args,
+      if (hipLaunchKernel(kern, dim3(grid_b), dim3(block), args,
                           balanced_lds<D, PAGED, XS>(prm, pl), stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     } else {
@@ -1545,10 +1586,8 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
     // (a range's tiles spread over that many shares), max_parts for fixed partitions
     int64_t per_head = pl.max_parts;
     if (pl.balanced) {
-      const int grid = balanced_grid<DT, D, PAGED, XS>(prm, pl);
-      if (grid <= 0) return GQA_ERR_LAUNCH;
       const int64_t ranges = std::max<int64_t>(1, (int64_t)prm.num_seqs * pl.n_groups);
-      per_head = (grid + ranges - 1) / ranges + 1;
+      per_head = (grid_b + ranges - 1) / ranges + 1;
     }
     const int64_t items = (int64_t)prm.num_seqs * prm.tq * prm.h_q;
     // Slots per head: enough that a slot folds at most two batches of partials
