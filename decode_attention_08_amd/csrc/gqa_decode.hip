@@ -901,10 +901,13 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
 // NT selects non-temporal K/V loads.  They raise the read rate when many
 // workgroups stream at once, but a lone wave that walks a whole long sequence
 // is latency-bound and runs faster with ordinary loads (the host decides).
+// SPLIT: a workgroup of hpw < 8 KV heads gives each head wph waves, which
+// split the partition's tiles (as in the balanced kernel).
 
-template <class DT, int D, bool PAGED, bool XS, bool NT>
+template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
+  __shared__ float2 mlx[SPLIT ? kMaxHeadsPerGroup * 16 : 1];         // sub-wave (m, l) exchange
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = blockIdx.x % a.max_parts;
   const int rest = blockIdx.x / a.max_parts;
@@ -916,10 +919,10 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
   if (p >= n_part) return;                       // uniform over the workgroup
   const int t0 = split ? p * a.part_size : 0;
   const int t1 = split ? min(t0 + a.part_size, L) : L;
-  const int j = hg * a.hpw + w;
+  const int j = hg * a.hpw + (SPLIT ? w % a.hpw : w);
   const int64_t row0 = ((int64_t)s * a.h_kv + j) * a.ncol;   // partial rows per (s, j, column)
-  wave_segment<DT, D, PAGED, XS, NT, false>(
-      a, smem, smem + (XS ? 0 : w * Geo<D>::V_TILE), nullptr, s, j, t0, t1, !split,
+  wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
+      a, smem, smem + ((XS && !SPLIT) ? 0 : w * Geo<D>::V_TILE), mlx, s, j, t0, t1, !split,
       a.part_ml + row0 * a.max_parts + p, a.max_parts, a.part_o + (row0 * a.max_parts + p) * D,
       (int64_t)a.max_parts * D);
 }
@@ -1333,6 +1336,9 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
 
 constexpr int32_t kDefaultV1Max = 256;
 constexpr int32_t kFallbackPartition = 512;
+// Fixed partitions: fewest work items (partition, head group, sequence) before
+// head groups are narrowed: one per CU of an MI355X.
+constexpr int64_t kFixedMinItems = 256;
 
 struct Problem {
   bool paged;
@@ -1406,8 +1412,11 @@ int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
   return (int64_t)num_seqs * n_groups * std::max<int64_t>(1, ((int64_t)max_ctx + kTile - 1) / kTile);
 }
 
+// parts_per_seq: partitions every sequence is known to have (1 unless a
+// contiguous cache is longer than v1_max_ctx); it only steers the head grouping
+// of the fixed scheduler, never the workspace size.
 Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
-               const gqa_policy_t& pol) {
+               const gqa_policy_t& pol, int64_t parts_per_seq = 1) {
   Plan pl{};
   pl.hpw = heads_per_group(h_kv, d);
   // a workgroup of fewer than the full complement of waves gives each KV head
@@ -1428,6 +1437,21 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
     pl.vc = (h_q / h_kv) * t_q <= 4 ? 4 : 8;
   pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
+  if (!pl.balanced) {
+    // A workgroup per (partition, head group, sequence).  With fewer work items
+    // than kFixedMinItems (e.g. 64 unsplit sequences of 8 KV heads: 64), narrow
+    // the head groups, down to one KV head per workgroup as the pages have it;
+    // a group of one or two heads gives each head several waves, which split
+    // its partition's tiles.
+    while (pl.hpw > 1 && (int64_t)num_seqs * parts_per_seq * (h_kv / pl.hpw) < kFixedMinItems) {
+      int h = pl.hpw - 1;
+      while (h > 1 && h_kv % h != 0) --h;
+      pl.hpw = h;
+    }
+    pl.n_groups = h_kv / pl.hpw;
+    // as in the balanced scheduler, only groups of one or two heads split
+    if (pl.hpw <= 2) pl.wph = max_heads_per_group(d) / pl.hpw;
+  }
   if (!pl.can_split) return pl;
   if (pl.balanced) {
     const size_t rows = (size_t)2 * kMaxGrid * pl.hpw * (h_q / h_kv) * t_q;
@@ -1573,9 +1597,13 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       // that is not split); a contiguous cache longer than v1_max_ctx splits
       // every sequence.
       const bool short_walks = prm.v1_max_ctx <= prm.part_size || (!PAGED && prm.s_kv > prm.v1_max_ctx);
+      const bool sw = pl.wph > 1;
       const void* kern =
-          short_walks ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true>)
-                      : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false>);
+          short_walks
+              ? (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true, true>)
+                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true, false>))
+              : (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false, true>)
+                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false, false>));
       if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(block), args, tiles_lds<D, XS>(pl),
                           stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
@@ -1659,7 +1687,11 @@ gqa_status_t run(const Problem& pb) {
   const int max_ctx = (int)max_ctx64;
   if ((pol.flags & GQA_POLICY_VALU_DOT2) && (pb.d != kDot2D || pb.xsplit || G * pb.tq > 8))
     return GQA_ERR_UNSUPPORTED;
-  const Plan pl = make_plan(pb.num_seqs, pb.tq, pb.h_q, pb.h_kv, pb.d, max_ctx, pol);
+  const int64_t parts_per_seq =
+      (!pb.paged && pol.partition_size > 0 && pb.s_kv > pol.v1_max_ctx)
+          ? ((int64_t)pb.s_kv + pol.partition_size - 1) / pol.partition_size
+          : 1;
+  const Plan pl = make_plan(pb.num_seqs, pb.tq, pb.h_q, pb.h_kv, pb.d, max_ctx, pol, parts_per_seq);
   if ((pol.flags & GQA_POLICY_VALU_DOT2) && !pl.balanced) return GQA_ERR_UNSUPPORTED;
   if (!pl.balanced && (int64_t)pl.max_parts * pl.n_groups * pb.num_seqs > INT32_MAX)
     return GQA_ERR_BAD_SHAPE;
