@@ -181,6 +181,18 @@ __device__ __forceinline__ T load_stream(const uint16_t* p) {
 // sequence still occupies one, so that exactly one workgroup writes its zero row)
 __device__ __forceinline__ int seq_tiles(int L) { return max(1, (L + kTile - 1) / kTile); }
 
+// Waits until every vector-memory operation of this wave has completed
+// (s_waitcnt vmcnt(0); the LDS/scalar and export counters are left alone).
+// The token loop calls it before issuing the next tile: on MI355X a wave with
+// two tiles of 16-byte loads outstanding (up to 32 per lane) streams slower
+// than one that keeps at most one tile (16) in flight, and the CU's other
+// waves cover the gap.
+__device__ __forceinline__ void wait_tile_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt 0, expcnt 7, lgkmcnt 15 (no wait)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Orders this wave's LDS stores before its later LDS loads (and vice versa):
 // the asm is a compiler memory barrier and the wait retires the wave's
 // outstanding LDS operations.  Each wave only touches its own LDS tile.
@@ -472,7 +484,8 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   //      state issues its loads unconditionally and the last one or two tiles
   //      are peeled, so every wait count the compiler derives is static; the
   //      scheduling barriers keep each prefetch ahead of the compute it
-  //      overlaps.
+  //      overlaps.  The current tile has landed before the next one is issued,
+  //      so a wave never has more than one tile of loads outstanding.
   int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   if constexpr (D > 128) {
     // d = 256: one register tile (32 KB of K/V per wave).  A wave waits for
@@ -487,9 +500,11 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
     int tb = t0;
     load(A, tb);
     while (n >= 3) {
+      wait_tile_loads();
       load(B, tb + kTile);
       __builtin_amdgcn_sched_barrier(0);
       compute(A, tb);
+      wait_tile_loads();
       load(A, tb + 2 * kTile);
       __builtin_amdgcn_sched_barrier(0);
       compute(B, tb + kTile);
@@ -497,6 +512,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
       n -= 2;
     }
     if (n == 2) {
+      wait_tile_loads();
       load(B, tb + kTile);
       __builtin_amdgcn_sched_barrier(0);
       compute(A, tb);
