@@ -285,11 +285,17 @@ def cpu_baseline(name: str, budget_s: float = 10.0):
             "seconds": round(t_used, 3)}
 
 
-def read_probe(reps: int = 10):
+def read_probe(reps: int = 10, sizes: dict | None = None):
     """Achievable HBM read rate: the streaming-read probe (libhbm_probe.so)
     reading a PROBE_BYTES buffer, `reps` launches back to back between HIP
     events on the launch stream; best over its access patterns (grid-stride;
-    chunked with 8, 16 or 32 loads in flight per lane) and grid sizes."""
+    chunked with 8, 16 or 32 loads in flight per lane) and grid sizes.
+
+    `sizes` ({name: bytes}) also times reads of exactly that many bytes, each
+    launch at the next disjoint offset of the buffer (as a decode step reads a
+    freshly rotated cache copy), chunked with 16 loads in flight and 1, 2, 4 or
+    8 workgroups per CU (best reported): the rate a bare streaming read of a
+    workload's K/V byte count reaches, fixed per-launch costs included."""
     import ctypes
     import torch
 
@@ -324,11 +330,35 @@ def read_probe(reps: int = 10):
             sweep[f"{names[mode]}/{per_cu}_per_cu"] = round(gbs, 1)
             if gbs > best[0]:
                 best = (gbs, grid, mode)
+    same = {}
+    for name, nbytes in (sizes or {}).items():
+        nbytes = nbytes // 4096 * 4096
+        regions = PROBE_BYTES // nbytes
+        if regions < 2:
+            continue
+        n_launch = min(reps * 2, regions)
+        top = 0.0
+        for per_cu in (1, 2, 4, 8):
+            def launch(i):
+                off = (i % regions) * nbytes
+                return lib.hbm_read_probe(buf.data_ptr() + off, nbytes, key, sink.data_ptr(),
+                                          cus * per_cu, 2, ctypes.c_void_p(stream.cuda_stream))
+            torch.cuda.synchronize()
+            assert launch(regions - 1) == 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n_launch):
+                assert launch(i) == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            top = max(top, nbytes * n_launch / (a.elapsed_time(b) * 1e-3) / 1e9)
+        same[name] = {"bytes": nbytes, "gbs": round(top, 1)}
     del buf, sink
     torch.cuda.empty_cache()
     return {"gbs": round(best[0], 1), "bytes": PROBE_BYTES, "grid": best[1],
             "pattern": names[best[2]],
             "pct_of_peak": round(100.0 * best[0] / PEAK_GBS, 2), "sweep": sweep,
+            "same_size": same,
             "method": "16-byte non-temporal loads, 256-lane workgroups; "
                       "mean over back-to-back launches between HIP events"}
 
@@ -505,7 +535,11 @@ def main():
                       f"partition {r['partition_us_mean']:.1f} us ({r['partition_gbs']:.0f} GB/s)",
                       file=sys.stderr, flush=True)
 
-    probe = None if args.no_also else read_probe()
+    sizes = {case.name: case.kv_bytes}
+    for k, r in also.items():
+        if k.endswith("/default") and not k.startswith("tiny_") and XSPLIT_SUFFIX not in k:
+            sizes[k.split("/")[0]] = r["kv_bytes"]
+    probe = None if args.no_also else read_probe(sizes=sizes)
     achieved = head["partition_gbs"]
     traffic, rocprof_us = traffic_for(case.name, args.policy)
     line = {
@@ -546,7 +580,10 @@ def main():
                      "valu_busy_pct": _round(traffic_record(case.name, args.policy).get("valu_busy_pct")),
                      "mfma_util_pct": _round(traffic_record(case.name, args.policy).get("mfma_util_pct")),
                      "merge_us_mean": round(head["merge_us_mean"], 3),
-                     "frac_of_read_probe": (round(achieved / probe["gbs"], 4) if probe else None)},
+                     "frac_of_read_probe": (round(achieved / probe["gbs"], 4) if probe else None),
+                     "frac_of_read_probe_same_size": (
+                         round(achieved / probe["same_size"][case.name]["gbs"], 4)
+                         if probe and case.name in probe["same_size"] else None)},
         "read_probe": probe,
         "cpu_baseline": cpu,
         "also": also,
