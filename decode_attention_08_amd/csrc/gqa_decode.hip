@@ -34,7 +34,9 @@
 // tile in LDS with coalesced 16-byte stores and reads it back transposed (the
 // x-split layout stores V transposed already).  Up to d = 128 every wave
 // keeps the next tile's K and V loads in flight while it computes the current
-// one.  K and V are read once, with non-temporal loads.
+// one, and issues them only once the current tile has landed (one tile of
+// loads outstanding per wave).  K and V are read once, with non-temporal
+// loads.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
