@@ -2,10 +2,10 @@
 //
 // Kernels:
 //   partition kernels  a workgroup holds the waves of a head group of HPW KV
-//                      heads (up to 8, up to 4 at d = 256; a group of one or
-//                      two heads gets several waves per head); all its waves
-//                      walk the same token segment of one sequence, so that
-//                      together they read whole K/V rows (the cache
+//                      heads (up to 4; a group of one or two heads gets
+//                      several waves per head); all its waves walk the same
+//                      token segment of one sequence, so that together they
+//                      read whole runs of a K/V row (the cache
 //                      interleaves the KV heads of a token).  For its KV head
 //                      a wave computes the partial triple (m, l, O) of the
 //                      G * T_q query rows sharing it (decode-long page, "Local
@@ -919,7 +919,7 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
 // NT selects non-temporal K/V loads.  They raise the read rate when many
 // workgroups stream at once, but a lone wave that walks a whole long sequence
 // is latency-bound and runs faster with ordinary loads (the host decides).
-// SPLIT: a workgroup of hpw < 8 KV heads gives each head wph waves, which
+// SPLIT: a workgroup of one or two KV heads gives each head wph waves, which
 // split the partition's tiles (as in the balanced kernel).
 
 template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
@@ -1404,10 +1404,16 @@ gqa_status_t resolve_policy(const gqa_policy_t* in, gqa_policy_t* out) {
 }
 
 // KV heads per workgroup: the largest divisor of h_kv that is at most
-// max_heads_per_group(d), so that a workgroup's waves read whole groups of
-// adjacent heads of a token.
+// kGroupHeads (and max_heads_per_group(d)), so that a workgroup's waves read
+// whole groups of adjacent heads of a token.  Four heads (1 KB of a 2 KB
+// token row at d = 128, one workgroup of four waves per CU) beat eight on
+// MI355X: a split range then spans half as many workgroups, so the launch
+// writes half the fp32 partials, whose dirty lines the L2s must write back
+// (contig_b8 step 29.6 -> 27.3 us, long_128k 92.9 -> 87.4 us, paged_b64
+// 167.2 -> 163.5 us).  Two heads per workgroup were slower again.
+constexpr int kGroupHeads = 4;
 int heads_per_group(int h_kv, int d) {
-  for (int h = std::min(h_kv, max_heads_per_group(d)); h > 1; --h)
+  for (int h = std::min({h_kv, kGroupHeads, max_heads_per_group(d)}); h > 1; --h)
     if (h_kv % h == 0) return h;
   return 1;
 }
@@ -1457,7 +1463,8 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
   if (!pl.balanced) {
     // A workgroup per (partition, head group, sequence).  With fewer work items
-    // than kFixedMinItems (e.g. 64 unsplit sequences of 8 KV heads: 64), narrow
+    // than kFixedMinItems (e.g. 64 unsplit sequences in two groups of four KV
+    // heads: 128), narrow
     // the head groups, down to one KV head per workgroup as the pages have it;
     // a group of one or two heads gives each head several waves, which split
     // its partition's tiles.

@@ -58,15 +58,18 @@ def test_workspace_size(gq):
     n = gq.workspace_size(4, 32, 8, 128, 8193, P)               # 17 partitions
     rows = 4 * 32 * 17
     assert n == ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
-    # balanced: a record per (sequence, head group of up to 8 KV heads) + two partial
+    # balanced: a record per (sequence, head group of up to 4 KV heads) + two partial
     # slots per workgroup (2048 workgroups at most), each holding the group's query heads
     B = gq.policy_default()
     assert gq.workspace_size(4, 32, 8, 128, B.v1_max_ctx, B) == 0
-    n = gq.workspace_size(4, 32, 8, 128, 4096, B)            # 8 KV heads: one group of 8
-    rows = 2 * 2048 * 32
+    n = gq.workspace_size(4, 32, 8, 128, 4096, B)            # 8 KV heads: two groups of 4
+    rows = 2 * 2048 * 4 * 4
     assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
-    n = gq.workspace_size(3, 48, 12, 64, 4096, B)             # 12 KV heads: two groups of 6
-    rows = 2 * 2048 * 6 * 4
+    n = gq.workspace_size(3, 48, 12, 64, 4096, B)             # 12 KV heads: three groups of 4
+    rows = 2 * 2048 * 4 * 4
+    assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 64 * 4
+    n = gq.workspace_size(2, 36, 6, 64, 4096, B)              # 6 KV heads: two groups of 3
+    rows = 2 * 2048 * 3 * 6
     assert n == 256 + ((rows * 8 + 255) // 256) * 256 + rows * 64 * 4
     n = gq.workspace_size(2, 16, 8, 256, 4096, B)             # d = 256: two groups of 4
     rows = 2 * 2048 * 4 * 2

@@ -33,7 +33,7 @@ def _valu(gq, **kw):
 
 
 @pytest.mark.parametrize("layout,dtype,h_kv,G,T", [
-    ("paged", W.F16, 8, 4, 1),        # 4 columns, 8 KV heads per workgroup
+    ("paged", W.F16, 8, 4, 1),        # 4 columns, two workgroups of 4 KV heads
     ("paged", W.BF16, 4, 8, 1),       # 8 columns
     ("paged", W.F16, 2, 1, 1),        # 1 column of 4; a group of two heads, one wave each
     ("paged", W.BF16, 3, 3, 2),       # 6 query rows of 8 (two tokens of three heads)
