@@ -254,34 +254,54 @@ def _cpu_worker(name: str, w: int, n: int, budget_s: float, barrier, results):
     results.put((done_bytes, done_pairs, elapsed))
 
 
+def _gpu_initialised() -> bool:
+    torch = sys.modules.get("torch")
+    return bool(torch is not None and torch.cuda.is_initialized())
+
+
 def cpu_baseline(name: str, budget_s: float = 10.0):
     """The float64 oracle, as it stands, on the workload `name`: a pool of
     worker processes (one per available core, at most CPU_WORKERS_MAX), each
     with one BLAS thread, over whole (sequence, KV head) slices for about
     budget_s of wall time.  Rate = all workers' K/V bytes / the longest
-    worker's time.  The workers are started fresh (spawn) and must be started
-    before this process uses the GPU."""
+    worker's time.  The workers are forked before this process uses the GPU
+    (spawned if it already has), and every one of them is joined, or
+    terminated, before this returns: no child process outlives the call."""
     import multiprocessing as mp
 
-    n = max(1, min(CPU_WORKERS_MAX, len(os.sched_getaffinity(0))))
-    ctx = mp.get_context("spawn")
+    available = len(os.sched_getaffinity(0))
+    n = max(1, min(CPU_WORKERS_MAX, available))
+    ctx = mp.get_context("spawn" if _gpu_initialised() else "fork")
     barrier = ctx.Barrier(n)
-    results = ctx.Queue()
+    results = ctx.SimpleQueue()               # no feeder thread to outlive the call
     procs = [ctx.Process(target=_cpu_worker, args=(name, w, n, budget_s, barrier, results))
              for w in range(n)]
-    for p in procs:
-        p.start()
-    got = [results.get(timeout=600) for _ in procs]
-    for p in procs:
-        p.join(timeout=60)
+    try:
+        for p in procs:
+            p.start()
+        got = [results.get() for _ in procs]
+    finally:
+        for p in procs:
+            if p.pid is not None:
+                p.join(timeout=30)
+        for p in procs:
+            if p.is_alive():
+                p.terminate()
+                p.join(timeout=10)
+        for p in procs:
+            if p.pid is not None:
+                p.close()
+        results.close()
     done_bytes = sum(g[0] for g in got)
     done_pairs = sum(g[1] for g in got)
     t_used = max(g[2] for g in got)
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+            "host_cores": os.cpu_count(), "available_cores": available,
             "sample": (f"{done_pairs} (sequence, KV head) slices of {name} over {n} worker "
                        f"processes (each every {n}-th slice of a seeded order, repeated), "
                        f"{done_bytes} K/V bytes in {t_used:.2f} s; float64 numpy oracle, one "
-                       f"BLAS thread per worker"),
+                       f"BLAS thread per worker; {available} cores available to the process, "
+                       f"{os.cpu_count()} on the host"),
             "seconds": round(t_used, 3)}
 
 

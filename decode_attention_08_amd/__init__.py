@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     policy_default,
     policy_pages,
     status_string,
+    check_block_table,
     workspace_size,
     EXPORTED_SYMBOLS,
     PreparedCall,

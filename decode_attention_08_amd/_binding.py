@@ -150,7 +150,11 @@ def _out(q, out):
 
 def _workspace(workspace, need, device, zeroed: bool = False):
     """The caller's workspace, or a new one (zero-filled when the policy's fused
-    merge needs its counters at zero before the first call)."""
+    merge needs its counters at zero before the first call).  prepare() makes
+    a new one while the launch stream is current, so that the caching
+    allocator ties it to that stream: it is then neither handed to another
+    stream's allocation while the launch may still use it, nor zero-filled on
+    another stream."""
     if need == 0:
         return None, 0
     if workspace is None:
@@ -158,6 +162,46 @@ def _workspace(workspace, need, device, zeroed: bool = False):
         workspace = alloc(need, dtype=torch.uint8, device=device)
     _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def _torch_stream(stream, device):
+    """The launch stream as a torch stream object (a raw hipStream_t handle is
+    wrapped), so that allocations for the call can be made on it."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    if int(stream) == 0:                          # the null stream is torch's default stream
+        return torch.cuda.default_stream(device)
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def check_block_table(block_table: torch.Tensor, ctx_lens: torch.Tensor, num_blocks: int,
+                      block_size: int) -> None:
+    """Checked mode for block ids, on a host copy, before anything is launched.
+
+    Token t of sequence s lives in block block_table[s, t // block_size]
+    (kernel-map page, "paged_attention_v1", the block-table addressing of its
+    key_cache).  Every entry the kernels will read (sequence s, entry e with
+    e < ceil(L_s / block_size), L_s = ctx_lens[s] clamped to
+    [0, max_blocks_per_seq * block_size] as the kernels clamp it) must name a
+    block of the pool: 0 <= id < num_blocks.  Raises ValueError naming the
+    first offending (sequence, entry, id).  Entries past a sequence's length
+    are never read and are not checked."""
+    import numpy as np
+    bt = block_table.detach().to("cpu").numpy()
+    lens = ctx_lens.detach().to("cpu").numpy().astype(np.int64)
+    _require(bt.ndim == 2 and lens.ndim == 1 and bt.shape[0] == lens.shape[0],
+             "block_table must be [num_seqs, max_blocks] and ctx_lens [num_seqs]")
+    max_blocks = bt.shape[1]
+    lens = lens.clip(0, max_blocks * block_size)
+    used = (lens + block_size - 1) // block_size
+    live = np.arange(max_blocks)[None, :] < used[:, None]
+    bad = live & ((bt < 0) | (bt >= num_blocks))
+    if bad.any():
+        s, e = (int(x) for x in np.argwhere(bad)[0])
+        raise ValueError(f"block_table[{s}, {e}] = {int(bt[s, e])} is outside the pool of "
+                         f"{num_blocks} blocks (sequence {s} reads {int(used[s])} blocks)")
 
 
 def _stream(stream, device):
@@ -218,6 +262,11 @@ class PreparedCall:
         self._ex = args.t_q != 1 or keep[0].dim() == 4
         self._keep = keep
 
+    @property
+    def out(self) -> torch.Tensor:
+        """The output tensor the call writes."""
+        return self._keep[5]
+
     def _invoke(self) -> int:
         a = self._a
         if self._ex:
@@ -246,11 +295,13 @@ class PreparedCall:
 
 def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
             workspace=None, policy: Optional[Policy] = None, stream=None,
-            xsplit: bool = False) -> PreparedCall:
+            xsplit: bool = False, check_blocks: bool = False) -> PreparedCall:
     """Validate once and return a PreparedCall.  Paged when block_table is
     given (the x-split pools with xsplit=True), contiguous otherwise.  q is
     [num_seqs, h_q, d] or, for t_q query tokens per sequence, [num_seqs, t_q,
-    h_q, d]; out has q's shape."""
+    h_q, d]; out has q's shape.  A new out or workspace is allocated on the
+    launch stream.  check_blocks=True first checks, on a host copy, that every
+    block id the call will read lies inside the pool (check_block_table)."""
     policy = policy_default() if policy is None else policy
     if block_table is None:
         _require(not xsplit, "the x-split layout is a paged layout (block_table required)")
@@ -258,20 +309,27 @@ def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
         _check_tensors(q, {"q": q, "k": k, "v": v})
     else:
         layout = GQA_KV_PAGED_XSPLIT if xsplit else GQA_KV_PAGED
+        if check_blocks:
+            _require(k.dim() >= 4, "paged k must be a block pool")
+            check_block_table(block_table, ctx_lens, int(k.shape[0]),
+                              int(k.shape[3] if xsplit else k.shape[1]))
         _check_tensors(q, {"q": q, "k_cache": k, "v_cache": v, "block_table": block_table,
                            "ctx_lens": ctx_lens})
-    out = _out(q, out)
     B, t_q, h_q, d, h_kv, s_kv, max_blocks, bs = _shapes(q, k, v, block_table, ctx_lens, layout)
+    launch_stream = _torch_stream(stream, q.device)
+    with torch.cuda.stream(launch_stream):
+        out = _out(q, out)
     a = DecodeArgs(layout=layout, dtype=_dtype_code(q), q=_ptr(q), k=_ptr(k), v=_ptr(v),
                    out=_ptr(out), block_table=_ptr(block_table), ctx_lens=_ptr(ctx_lens),
                    num_seqs=B, t_q=t_q, h_q=h_q, h_kv=h_kv, d_head=d, s_kv=s_kv,
                    max_blocks_per_seq=max_blocks, block_size=bs,
                    scale=1.0 / math.sqrt(d) if scale is None else float(scale),
-                   stream=_stream(stream, q.device))
+                   stream=launch_stream.cuda_stream)
     a.policy = ctypes.pointer(policy)
     need = int(lib.gqa_decode_ex_workspace_size(ctypes.byref(a)))
-    workspace, ws_bytes = _workspace(workspace, need, q.device,
-                                     zeroed=bool(policy.flags & GQA_POLICY_FUSED_MERGE))
+    with torch.cuda.stream(launch_stream):
+        workspace, ws_bytes = _workspace(workspace, need, q.device,
+                                         zeroed=bool(policy.flags & GQA_POLICY_FUSED_MERGE))
     a.workspace = _ptr(workspace)
     a.workspace_bytes = ws_bytes
     return PreparedCall(layout, a, policy, (q, k, v, block_table, ctx_lens, out, workspace))
@@ -280,11 +338,14 @@ def prepare(q, k, v, *, block_table=None, ctx_lens=None, scale=None, out=None,
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            block_table: torch.Tensor, ctx_lens: torch.Tensor, *, scale: Optional[float] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           policy: Optional[Policy] = None, stream=None) -> torch.Tensor:
+           policy: Optional[Policy] = None, stream=None,
+           check_blocks: bool = False) -> torch.Tensor:
     """Paged GQA decode: q [B, h_q, d] (or [B, t_q, h_q, d]), k/v [num_blocks, bs, h_kv, d],
-    block_table [B, max_blocks] int32, ctx_lens [B] int32 -> out of q's shape."""
+    block_table [B, max_blocks] int32, ctx_lens [B] int32 -> out of q's shape.
+    check_blocks=True rejects out-of-pool block ids on the host first."""
     call = prepare(q, k_cache, v_cache, block_table=block_table, ctx_lens=ctx_lens, scale=scale,
-                   out=out, workspace=workspace, policy=policy, stream=stream)
+                   out=out, workspace=workspace, policy=policy, stream=stream,
+                   check_blocks=check_blocks)
     call()
     return call._keep[5]
 
@@ -293,11 +354,12 @@ def decode_xsplit(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   block_table: torch.Tensor, ctx_lens: torch.Tensor, *,
                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, policy: Optional[Policy] = None,
-                  stream=None) -> torch.Tensor:
+                  stream=None, check_blocks: bool = False) -> torch.Tensor:
     """Paged GQA decode over the x-split layout: k [num_blocks, h_kv, d/8, bs, 8],
     v [num_blocks, h_kv, d, bs]; otherwise as decode()."""
     call = prepare(q, k_cache, v_cache, block_table=block_table, ctx_lens=ctx_lens, scale=scale,
-                   out=out, workspace=workspace, policy=policy, stream=stream, xsplit=True)
+                   out=out, workspace=workspace, policy=policy, stream=stream, xsplit=True,
+                   check_blocks=check_blocks)
     call()
     return call._keep[5]
 

@@ -71,3 +71,16 @@ def test_read_probe_library_validates_arguments():
         assert f(0x10008, 1 << 20, 0, 0x20000, 64, mode, None) == 1   # misaligned
     assert f(0x10000, 1 << 20, 0, 0x20000, 64, 4, None) == 1          # unknown pattern
     assert f(0x10000, 1 << 20, 0, 0x20000, 64, -1, None) == 1         # unknown pattern
+
+
+def test_cpu_baseline_leaves_no_child_process():
+    import multiprocessing
+    import psutil
+    import bench
+    before = {c.pid for c in psutil.Process().children(recursive=True)}
+    rec = bench.cpu_baseline("tiny_contig", budget_s=0.2)
+    assert rec["available_cores"] >= rec["cores"] >= 1
+    assert rec["host_cores"] >= rec["available_cores"]
+    assert not multiprocessing.active_children()
+    after = {c.pid for c in psutil.Process().children(recursive=True)}
+    assert after <= before, after - before

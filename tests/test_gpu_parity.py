@@ -216,8 +216,9 @@ def test_named_workloads_sampled(gq, name):
 @pytest.mark.parametrize("h_kv,G,d", [(12, 2, 64), (16, 1, 128), (6, 3, 128), (2, 16, 64),
                                       (4, 3, 256), (8, 2, 256), (6, 1, 256), (2, 16, 256)])
 def test_head_groups(gq, h_kv, G, d):
-    """KV heads per workgroup = largest divisor of h_kv up to 8, up to 4 at d = 256
-    (12 -> 6, 16 -> 8, 6 -> 6; at d = 256: 4 -> 4, 8 -> 4, 6 -> 3, 2 -> 2)."""
+    """KV heads per workgroup = largest divisor of h_kv up to 4 (12 -> 4, 16 -> 4,
+    6 -> 3, 2 -> 2, 4 -> 4, 8 -> 4); groups of one or two heads give each head
+    several waves."""
     case = W.paged_case(f"hg{h_kv}", 1200 + h_kv, [1300, 5, 333], h_q=G * h_kv, h_kv=h_kv, d=d,
                         dtype=W.BF16, extra_blocks=1)
     ref = R.decode(case)
@@ -346,3 +347,50 @@ def test_concurrent_streams(gq):
     for oa, ob in outs:
         assert np.array_equal(oa.float().cpu().numpy().astype(np.float64), want_a)
         assert np.array_equal(ob.float().cpu().numpy().astype(np.float64), want_b)
+
+
+def test_checked_block_ids_same_result(gq):
+    """check_blocks=True only adds the host check: same output bit for bit."""
+    case = W.paged_case("chk", 1900, [700, 1, 9000], h_q=16, h_kv=4, d=128, dtype=W.F16,
+                        extra_blocks=2)
+    dev = case_to_device(case, DEV)
+    want = run_case(dev)
+    got = gq.decode(dev["q"], dev["k"], dev["v"], dev["block_table"], dev["ctx_lens"],
+                    scale=case.scale, check_blocks=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.float().cpu().numpy().astype(np.float64), want)
+    bad = dev["block_table"].clone()
+    bad[2, 3] = case.k.shape[0]
+    with pytest.raises(ValueError, match="outside the pool"):
+        gq.decode(dev["q"], dev["k"], dev["v"], bad, dev["ctx_lens"], check_blocks=True)
+
+
+def test_side_stream_calls_keep_their_workspace(gq):
+    """One-shot calls on a side stream drop their workspace on return while the
+    launch may still be queued.  The binding allocates it on the launch stream,
+    so allocations and writes on the current stream meanwhile cannot reuse it."""
+    case = W.paged_case("side", 2000, [9000, 4000, 300, 12000], h_q=32, h_kv=8, d=128,
+                        dtype=W.F16)
+    dev = case_to_device(case, DEV)
+    want = run_case(dev)
+    pol = gq.policy_default(v1_max_ctx=0)          # every range split: partials in the workspace
+    want_split = run_case(dev, policy=pol)
+    need = gq.workspace_size(case.num_seqs, case.h_q, case.h_kv, case.d,
+                             case.max_blocks * case.block_size, pol)
+    assert need > 0
+    side = torch.cuda.Stream(device=DEV)
+    outs = []
+    for rep in range(4):
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(20_000_000)            # keeps the side stream busy (bounded)
+        outs.append(gq.decode(dev["q"], dev["k"], dev["v"], dev["block_table"], dev["ctx_lens"],
+                              scale=case.scale, policy=pol, stream=side))
+        junk = torch.empty(need, dtype=torch.uint8, device=DEV)   # current stream
+        junk.fill_(0xFF)                             # NaN bit patterns if it aliased
+        del junk
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.float().cpu().numpy().astype(np.float64), want_split)
+    ref = R.decode(case)
+    assert_close(want_split, ref, W.F16, what="side stream, all split")
+    assert_close(want, ref, W.F16, what="side stream, default")
