@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     Policy,
     decode,
     decode_contiguous,
+    decode_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     decode_xsplit,
     X,
     lib,

@@ -26,8 +26,10 @@ GQA_KV_PAGED = 1
 GQA_KV_PAGED_XSPLIT = 2
 
 EXPORTED_SYMBOLS = ("gqa_policy_default", "gqa_policy_pages", "gqa_decode_workspace_size",
-                    "gqa_decode", "gqa_decode_xsplit", "gqa_decode_contiguous",
-                    "gqa_decode_ex", "gqa_decode_ex_workspace_size", "gqa_status_string")
+                    "gqa_decode", "gqa_decode_xsplit", "gqa_decode_noalloc",
+                    "gqa_decode_contiguous", "gqa_decode_ex", "gqa_decode_ex_workspace_size",
+                    "gqa_status_string")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GQA_NOALLOC_SCRATCH_BYTES of the header
 X = 8   # elements per 16-byte vector of the x-split K layout
 
 
@@ -69,6 +71,9 @@ lib.gqa_decode.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctype
 lib.gqa_decode.restype = _I
 lib.gqa_decode_xsplit.argtypes = lib.gqa_decode.argtypes
 lib.gqa_decode_xsplit.restype = _I
+lib.gqa_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                   ctypes.c_float, _I, ctypes.POINTER(Policy), _P]
+lib.gqa_decode_noalloc.restype = _I
 lib.gqa_decode_contiguous.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                       _P, ctypes.c_size_t, ctypes.POINTER(Policy), _P]
 lib.gqa_decode_contiguous.restype = _I
@@ -374,3 +379,30 @@ def decode_contiguous(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                    stream=stream)
     call()
     return call._keep[5]
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_table: torch.Tensor, ctx_lens: torch.Tensor, out: torch.Tensor, *,
+                   scale: Optional[float] = None, policy: Optional[Policy] = None,
+                   stream=None, check_blocks: bool = False) -> torch.Tensor:
+    """Paged GQA decode through gqa_decode_noalloc: as decode(), but the
+    library keeps the partials in its static per-device scratch, so neither
+    the C call nor this wrapper allocates (out is the caller's).  Calls that
+    overlap on one device race on the scratch."""
+    _require(q.dim() == 3, "gqa_decode_noalloc takes q [num_seqs, h_q, d_head]")
+    if check_blocks:
+        check_block_table(block_table, ctx_lens, int(k_cache.shape[0]), int(k_cache.shape[1]))
+    _check_tensors(q, {"q": q, "k_cache": k_cache, "v_cache": v_cache,
+                       "block_table": block_table, "ctx_lens": ctx_lens, "out": out})
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    B, _, h_q, d, h_kv, _, max_blocks, bs = _shapes(q, k_cache, v_cache, block_table, ctx_lens,
+                                                    GQA_KV_PAGED)
+    policy = policy_default() if policy is None else policy
+    st = lib.gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                block_table.data_ptr(), ctx_lens.data_ptr(), out.data_ptr(),
+                                B, max_blocks, h_q, h_kv, d, bs,
+                                1.0 / math.sqrt(d) if scale is None else float(scale),
+                                _dtype_code(q), ctypes.byref(policy), _stream(stream, q.device))
+    if st != 0:
+        raise GqaError(st)
+    return out

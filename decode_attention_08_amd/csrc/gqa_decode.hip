@@ -1352,6 +1352,33 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
 
 // ------------------------------------------------------------------ host --
 
+// The device's scratch for gqa_decode_noalloc: partial triples and range
+// records of the split sequences, GQA_NOALLOC_SCRATCH_BYTES per device, held
+// by every device the library runs on until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: host code
+// uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device.
+gqa_status_t scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return GQA_ERR_LAUNCH;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return GQA_OK;
+}
+
 constexpr int32_t kDefaultV1Max = 256;
 constexpr int32_t kFallbackPartition = 512;
 // Fixed partitions: fewest work items (partition, head group, sequence) before
@@ -1381,6 +1408,7 @@ struct Problem {
   size_t ws_bytes;
   const gqa_policy_t* policy;
   void* stream;
+  bool noalloc;       // workspace: the device's static scratch (gqa_decode_noalloc)
 };
 
 bool aligned(const void* ptr, uintptr_t n) { return (reinterpret_cast<uintptr_t>(ptr) & (n - 1)) == 0; }
@@ -1436,6 +1464,34 @@ int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
   return (int64_t)num_seqs * n_groups * std::max<int64_t>(1, ((int64_t)max_ctx + kTile - 1) / kTile);
 }
 
+// Byte sizes of the workspace regions.  The balanced decomposition gives each
+// of its (at most grid_rows) workgroups two partial slots; the fixed one a
+// slot per (sequence, query row, partition).
+void size_workspace(Plan& pl, int num_seqs, int t_q, int h_q, int h_kv, int d, int64_t grid_rows) {
+  if (pl.balanced) {
+    const size_t rows = (size_t)2 * grid_rows * pl.hpw * (h_q / h_kv) * t_q;
+    pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
+    pl.ws_cnt = pl.fused ? align256((size_t)num_seqs * pl.n_groups * sizeof(int)) : 0;
+    pl.ws_ml = align256(rows * sizeof(float2));
+    pl.ws_o = rows * (size_t)d * sizeof(float);
+  } else {
+    const size_t rows = (size_t)num_seqs * h_q * t_q * pl.max_parts;
+    pl.ws_desc = 0;
+    pl.ws_cnt = 0;
+    pl.ws_ml = align256(rows * sizeof(float2));
+    pl.ws_o = rows * (size_t)d * sizeof(float);
+  }
+  pl.ws_total = pl.ws_desc + pl.ws_cnt + pl.ws_ml + pl.ws_o;
+}
+
+// Points the Params' workspace regions into ws (laid out as size_workspace says).
+void place_workspace(Params& prm, const Plan& pl, char* ws) {
+  prm.desc = pl.ws_desc ? reinterpret_cast<int4*>(ws) : nullptr;
+  prm.cnt = pl.ws_cnt ? reinterpret_cast<int*>(ws + pl.ws_desc) : nullptr;
+  prm.part_ml = reinterpret_cast<float2*>(ws + pl.ws_desc + pl.ws_cnt);
+  prm.part_o = reinterpret_cast<float*>(ws + pl.ws_desc + pl.ws_cnt + pl.ws_ml);
+}
+
 // parts_per_seq: partitions every sequence is known to have (1 unless a
 // contiguous cache is longer than v1_max_ctx); it only steers the head grouping
 // of the fixed scheduler, never the workspace size.
@@ -1478,20 +1534,8 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
     if (pl.hpw <= 2) pl.wph = max_heads_per_group(d) / pl.hpw;
   }
   if (!pl.can_split) return pl;
-  if (pl.balanced) {
-    const size_t rows = (size_t)2 * kMaxGrid * pl.hpw * (h_q / h_kv) * t_q;
-    pl.fused = (pol.flags & GQA_POLICY_FUSED_MERGE) != 0;
-    pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
-    pl.ws_cnt = pl.fused ? align256((size_t)num_seqs * pl.n_groups * sizeof(int)) : 0;
-    pl.ws_ml = align256(rows * sizeof(float2));
-    pl.ws_o = rows * (size_t)d * sizeof(float);
-  } else {
-    const size_t rows = (size_t)num_seqs * h_q * t_q * pl.max_parts;
-    pl.ws_desc = 0;
-    pl.ws_ml = align256(rows * sizeof(float2));
-    pl.ws_o = rows * (size_t)d * sizeof(float);
-  }
-  pl.ws_total = pl.ws_desc + pl.ws_cnt + pl.ws_ml + pl.ws_o;
+  pl.fused = pl.balanced && (pol.flags & GQA_POLICY_FUSED_MERGE) != 0;
+  size_workspace(pl, num_seqs, t_q, h_q, h_kv, d, kMaxGrid);
   return pl;
 }
 
@@ -1586,8 +1630,11 @@ gqa_status_t launch_merge(bool balanced, int64_t items, void** args, hipStream_t
   return GQA_OK;
 }
 
+// scratch: non-null for gqa_decode_noalloc, the device address of the static
+// scratch array; the workspace is then sized for the actual grid and placed there.
 template <class DT, int D, bool PAGED, bool XS>
-gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStream_t stream) {
+gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStream_t stream,
+                          char* scratch) {
   Params local = prm;
   void* args[] = {&local};
   const int block = 64 * pl.hpw * pl.wph;
@@ -1595,6 +1642,15 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
   if (pl.balanced) {
     grid_b = balanced_grid<DT, D, PAGED, XS>(prm, pl);
     if (grid_b <= 0) return GQA_ERR_LAUNCH;
+  }
+  if (scratch && pl.can_split) {
+    Plan sized = pl;
+    if (pl.balanced)
+      size_workspace(sized, prm.num_seqs, prm.tq, prm.h_q, prm.h_kv, D, grid_b);
+    if (sized.ws_total > kScratchBytes) return GQA_ERR_WORKSPACE;
+    place_workspace(local, sized, scratch);
+  }
+  if (pl.balanced) {
     if (!PAGED) {
       // the share size the partition kernel derives, for the merge kernel
       const int64_t total = (int64_t)prm.num_seqs * pl.n_groups *
@@ -1673,18 +1729,18 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
 
 template <class DT, int D>
 gqa_status_t launch_layout(const Problem& pb, const Params& prm, const Plan& pl, int ph,
-                           hipStream_t st) {
-  if (pb.xsplit) return launch_typed<DT, D, true, true>(prm, pl, ph, st);
-  return pb.paged ? launch_typed<DT, D, true, false>(prm, pl, ph, st)
-                  : launch_typed<DT, D, false, false>(prm, pl, ph, st);
+                           hipStream_t st, char* scr) {
+  if (pb.xsplit) return launch_typed<DT, D, true, true>(prm, pl, ph, st, scr);
+  return pb.paged ? launch_typed<DT, D, true, false>(prm, pl, ph, st, scr)
+                  : launch_typed<DT, D, false, false>(prm, pl, ph, st, scr);
 }
 
 template <class DT>
 gqa_status_t launch_dtype(const Problem& pb, const Params& prm, const Plan& pl, int ph,
-                          hipStream_t st) {
-  if (pb.d == 64) return launch_layout<DT, 64>(pb, prm, pl, ph, st);
-  if (pb.d == 128) return launch_layout<DT, 128>(pb, prm, pl, ph, st);
-  return launch_layout<DT, 256>(pb, prm, pl, ph, st);
+                          hipStream_t st, char* scr) {
+  if (pb.d == 64) return launch_layout<DT, 64>(pb, prm, pl, ph, st, scr);
+  if (pb.d == 128) return launch_layout<DT, 128>(pb, prm, pl, ph, st, scr);
+  return launch_layout<DT, 256>(pb, prm, pl, ph, st, scr);
 }
 
 gqa_status_t run(const Problem& pb) {
@@ -1732,7 +1788,12 @@ gqa_status_t run(const Problem& pb) {
     return GQA_ERR_MISALIGNED;
   if (pb.paged && (!aligned(pb.block_table, 4) || !aligned(pb.ctx_lens, 4)))
     return GQA_ERR_MISALIGNED;
-  if (pl.ws_total > 0) {
+  if (pb.noalloc) {
+    // the workspace is the device's static scratch; the fused merge's counters
+    // would need it zeroed first, so that flag is not offered here
+    if (pol.flags & GQA_POLICY_FUSED_MERGE) return GQA_ERR_UNSUPPORTED;
+    if (!pl.balanced && pl.ws_total > kScratchBytes) return GQA_ERR_WORKSPACE;
+  } else if (pl.ws_total > 0) {
     if (!pb.ws || pb.ws_bytes < pl.ws_total) return GQA_ERR_WORKSPACE;
     if (!aligned(pb.ws, 256)) return GQA_ERR_MISALIGNED;
   }
@@ -1745,13 +1806,7 @@ gqa_status_t run(const Problem& pb) {
   prm.out = static_cast<uint16_t*>(pb.out);
   prm.block_table = pb.block_table;
   prm.ctx_lens = pb.ctx_lens;
-  if (pl.ws_total > 0) {
-    char* ws = static_cast<char*>(pb.ws);
-    prm.desc = pl.ws_desc ? reinterpret_cast<int4*>(ws) : nullptr;
-    prm.cnt = pl.ws_cnt ? reinterpret_cast<int*>(ws + pl.ws_desc) : nullptr;
-    prm.part_ml = reinterpret_cast<float2*>(ws + pl.ws_desc + pl.ws_cnt);
-    prm.part_o = reinterpret_cast<float*>(ws + pl.ws_desc + pl.ws_cnt + pl.ws_ml);
-  }
+  if (pl.ws_total > 0 && !pb.noalloc) place_workspace(prm, pl, static_cast<char*>(pb.ws));
   prm.num_seqs = pb.num_seqs;
   prm.h_q = pb.h_q;
   prm.h_kv = pb.h_kv;
@@ -1771,11 +1826,18 @@ gqa_status_t run(const Problem& pb) {
   prm.max_parts = pl.max_parts;
   prm.c = pb.scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(pb.stream);
-  if (pb.dtype == GQA_F16) return launch_dtype<F16>(pb, prm, pl, pol.phases, st);
-  return launch_dtype<BF16>(pb, prm, pl, pol.phases, st);
+  char* scr = nullptr;
+  if (pb.noalloc) {
+    void* addr = nullptr;
+    const gqa_status_t ss = scratch_address(&addr);
+    if (ss != GQA_OK) return ss;
+    scr = static_cast<char*>(addr);
+  }
+  if (pb.dtype == GQA_F16) return launch_dtype<F16>(pb, prm, pl, pol.phases, st, scr);
+  return launch_dtype<BF16>(pb, prm, pl, pol.phases, st, scr);
 }
 
-gqa_status_t run_paged(bool xsplit, const void* q, const void* k_cache, const void* v_cache,
+gqa_status_t run_paged(bool xsplit, bool noalloc, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, const int32_t* ctx_lens, void* out,
                        int num_seqs, int max_blocks_per_seq, int h_q, int h_kv, int d_head,
                        int block_size, float scale, gqa_dtype_t dtype, void* workspace,
@@ -1783,6 +1845,7 @@ gqa_status_t run_paged(bool xsplit, const void* q, const void* k_cache, const vo
   Problem pb{};
   pb.paged = true;
   pb.xsplit = xsplit;
+  pb.noalloc = noalloc;
   pb.tq = 1;
   pb.q = q;
   pb.k = k_cache;
@@ -1840,7 +1903,7 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                         int d_head, int block_size, float scale, gqa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes,
                         const gqa_policy_t* policy, void* stream) {
-  return run_paged(false, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
+  return run_paged(false, false, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
                    max_blocks_per_seq, h_q, h_kv, d_head, block_size, scale, dtype, workspace,
                    workspace_bytes, policy, stream);
 }
@@ -1851,9 +1914,19 @@ gqa_status_t gqa_decode_xsplit(const void* q, const void* k_cache, const void* v
                                int d_head, int block_size, float scale, gqa_dtype_t dtype,
                                void* workspace, size_t workspace_bytes,
                                const gqa_policy_t* policy, void* stream) {
-  return run_paged(true, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
+  return run_paged(true, false, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
                    max_blocks_per_seq, h_q, h_kv, d_head, block_size, scale, dtype, workspace,
                    workspace_bytes, policy, stream);
+}
+
+gqa_status_t gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* ctx_lens, void* out,
+                                int num_seqs, int max_blocks_per_seq, int h_q, int h_kv,
+                                int d_head, int block_size, float scale, gqa_dtype_t dtype,
+                                const gqa_policy_t* policy, void* stream) {
+  return run_paged(false, true, q, k_cache, v_cache, block_table, ctx_lens, out, num_seqs,
+                   max_blocks_per_seq, h_q, h_kv, d_head, block_size, scale, dtype, nullptr, 0,
+                   policy, stream);
 }
 
 gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, void* out,
@@ -1940,7 +2013,7 @@ const char* gqa_status_string(gqa_status_t status) {
     case GQA_ERR_BAD_SHAPE: return "GQA_ERR_BAD_SHAPE: invalid or inconsistent sizes";
     case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: d_head, group size, block size or dtype not supported";
     case GQA_ERR_MISALIGNED: return "GQA_ERR_MISALIGNED: pointer alignment requirement not met";
-    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small (gqa_decode_noalloc: more than its static scratch)";
     case GQA_ERR_BAD_POLICY: return "GQA_ERR_BAD_POLICY: policy fields out of range";
     case GQA_ERR_BAD_SCALE: return "GQA_ERR_BAD_SCALE: scale is not finite";
     case GQA_ERR_LAUNCH: return "GQA_ERR_LAUNCH: kernel launch failed";

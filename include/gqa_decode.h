@@ -38,10 +38,10 @@
  * partials and the merge are fp32; the output is rounded to nearest-even.
  *
  * Ownership.  The caller owns every buffer, the workspace included.  The
- * library never allocates, frees or synchronises and keeps no device state
- * (it caches, per device and kernel, how many workgroups fit on the device
- * at once); calls on different streams with distinct workspaces and outputs
- * may run concurrently.
+ * library never allocates, frees or synchronises; its only device state is
+ * the static scratch of gqa_decode_noalloc (it also caches, per device and
+ * kernel, how many workgroups fit on the device at once).  Calls on different
+ * streams with distinct workspaces and outputs may run concurrently.
  *
  * Errors.  Every argument is checked on the host before any HIP call; a
  * failed check returns its status with nothing launched.  A failed launch
@@ -74,7 +74,8 @@ typedef enum gqa_status {
   GQA_ERR_BAD_SHAPE = 2,    /* a size is negative, zero where it may not be, or inconsistent */
   GQA_ERR_UNSUPPORTED = 3,  /* valid but not built: d_head, G, block_size or dtype */
   GQA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment stated above */
-  GQA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than gqa_decode_workspace_size() */
+  GQA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than gqa_decode_workspace_size(),
+                               or more than gqa_decode_noalloc's static scratch */
   GQA_ERR_BAD_POLICY = 6,   /* policy fields out of range */
   GQA_ERR_BAD_SCALE = 7,    /* scale is NaN or infinite */
   GQA_ERR_LAUNCH = 8        /* the HIP runtime refused a kernel launch */
@@ -188,6 +189,40 @@ gqa_status_t gqa_decode_xsplit(const void* q, const void* k_cache, const void* v
                                int d_head, int block_size, float scale, gqa_dtype_t dtype,
                                void* workspace, size_t workspace_bytes,
                                const gqa_policy_t* policy, void* stream);
+
+/*
+ * Allocation-free paged decode, for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Arguments, layouts, numerics and errors
+ * are those of gqa_decode, without the workspace: the partial triples and
+ * range records live in a static device array of GQA_NOALLOC_SCRATCH_BYTES
+ * that the library defines, one per device (each device the library runs on
+ * holds it until the process ends).  The call allocates and frees nothing;
+ * the caller still passes the inputs and out.
+ *
+ *  - The scratch needed is sized for the grid the call actually launches.
+ *    With the default policy that is (2 x workgroups x heads per workgroup x
+ *    G) rows of (d_head + 2) floats plus 16 bytes per (sequence, head group),
+ *    about 17 MB at d_head = 128 and 34 MB at 256 on an MI355X.  A call that
+ *    needs more (for instance the fixed policy of gqa_policy_pages() on a
+ *    large batch) returns GQA_ERR_WORKSPACE and launches nothing.
+ *  - GQA_POLICY_FUSED_MERGE returns GQA_ERR_UNSUPPORTED (its counters would
+ *    have to start at zero).  Nothing else in the scratch needs clearing:
+ *    every call writes the partials and records it reads.
+ *  - All calls on one device share its scratch, which keeps the last call's
+ *    contents (a phases = 2 call merges what the last phases = 1 call left).
+ *    Calls that overlap on one device race: serialise them, for instance by
+ *    issuing them on one stream.
+ *  - The first call on a device looks up the scratch's device address
+ *    (hipGetSymbolAddress); a failure there returns GQA_ERR_LAUNCH.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gqa_status_t gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* ctx_lens, void* out,
+                                int num_seqs, int max_blocks_per_seq, int h_q, int h_kv,
+                                int d_head, int block_size, float scale, gqa_dtype_t dtype,
+                                const gqa_policy_t* policy, void* stream);
 
 /*
  * Contiguous decode: every sequence holds s_kv tokens (s_kv >= 0) in a
