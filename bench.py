@@ -2,23 +2,28 @@
 
 One step = one pass of the whole decode path (partition kernel + merge kernel)
 over one batch of synthetic inputs already resident in HBM.  The timed steps
-are captured in a HIP graph and replayed between two synchronisations.  K/V are cycled
-over enough device copies (>= 1 GiB in total, i.e. more than four times the
-256 MB Infinity Cache) that no step can be served from the cache a previous
-step filled.
+are captured in a HIP graph; a bounded spin kernel keeps the stream busy while
+the host submits the replay, and a HIP event pair on the launch stream around
+the replay times the steps themselves (both sides bracketed by
+synchronisations).  The output after the timed replay must equal an eager
+step's bit for bit.  K/V are cycled over enough device copies (>= 1 GiB in
+total, i.e. more than four times the 256 MB Infinity Cache) that no step can be
+served from the cache a previous step filled.
 
-Prints ONE JSON line.  `value` is K+V GB/s of the headline workload
-(algorithmic K+V bytes / wall time per step between synchronisations);
-`roofline` gives the partition kernel's own HBM roofline fraction, its mean
-launch duration timed with HIP events on the launch stream around the timed
-steps' partition launches issued back to back, and its fraction of the
+Prints ONE JSON line.  The headline workload is mixed_b256, the largest
+configuration (256 sequences of log-normal lengths, both single-pass and split
+sequences in one batch).  `value` is its K+V GB/s (algorithmic K+V bytes / time
+per step); `roofline` gives the partition kernel's own HBM roofline fraction,
+its mean launch duration timed with HIP events on the launch stream around the
+timed steps' partition launches issued back to back, and its fraction of the
 achievable read rate a streaming-read probe measures (`read_probe`, context
 beside the published peak); `warm` repeats the steps on one K/V copy (no
-rotation), labelled as such and never the headline; `cpu_baseline` times the float64 oracle on a
-bounded sample of the same workload, in a pool of worker processes; `also`
-carries the other full-size workloads.
+rotation), labelled as such and never the headline; `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload, in a pool of worker
+processes; `also` carries the other full-size workloads and policies, each with
+a roofline object of its own.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload contig_b8]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload mixed_b256]
   python bench.py --summarize-rocprof DIR     # rocprofv3 csv -> short text
 """
 from __future__ import annotations
@@ -38,7 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "K/V HBM GB/s (and % of peak) + decode attention µs/step, 1 GPU"
 PEAK_GBS = 8000.0                       # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30                  # K/V bytes cycled per step sequence
-HEADLINE = "contig_b8"
+HEADLINE = "mixed_b256"            # the largest configuration (256 sequences, mixed lengths)
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_08_amd", "csrc", "gqa_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PROBE_LIB = os.path.join(ROOT, "decode_attention_08_amd", "libhbm_probe.so")
@@ -139,23 +144,41 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
         for i in range(warmup):
             call(ks[i % copies], vs[i % copies], phases=3)
         torch.cuda.synchronize()
+        eager = call.out.clone()                     # every K/V copy holds the same values
 
-        # ---- pass 1: graph replay of the timed steps
+        # ---- pass 1: graph replay of the timed steps.  A bounded spin kernel
+        # first keeps the stream busy while the host submits the replay, so the
+        # event pair around it times the steps alone, not the submission: the
+        # per-step figure does not depend on how many steps are timed.
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for i in range(steps):
                 call(ks[(warmup + i) % copies], vs[(warmup + i) % copies], phases=3)
         graph.replay()                               # first replay: not timed
         torch.cuda.synchronize()
+        call.out.fill_(float("nan"))
+        spin = _spin_cycles(torch, stream, seconds=2e-3)
         ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        torch.cuda._sleep(spin)
         ev_a.record(stream)
         graph.replay()
         ev_b.record(stream)
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / steps
+        wall_spin = time.perf_counter() - t0
         gpu_step = ev_a.elapsed_time(ev_b) * 1e-3 / steps
+        # the timed steps computed what an eager step computes, bit for bit
+        replay_matches = bool(torch.equal(call.out, eager))
+        if not replay_matches:
+            raise RuntimeError(f"{case.name}/{policy_name}: output after the timed replay "
+                               "differs from the eager step's")
+        # the same replay with no spin in front (wall clock, submission included)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
         del graph
 
         # ---- pass 1b (warm, reported as such, never the headline): the same
@@ -212,9 +235,11 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     res = {"workload": case.name, "policy": policy_name,
            "partition_size": pol.partition_size, "v1_max_ctx": pol.v1_max_ctx,
            "kv_bytes": case.kv_bytes, "copies": copies,
-           "ms_per_step": wall * 1e3, "us_per_step": wall * 1e6,
-           "us_per_step_gpu": gpu_step * 1e6,
-           "gbs": case.kv_bytes / wall / 1e9,
+           "ms_per_step": gpu_step * 1e3, "us_per_step": gpu_step * 1e6,
+           "gbs": case.kv_bytes / gpu_step / 1e9,
+           "wall_us_per_step": wall * 1e6,
+           "wall_with_spin_s": wall_spin,
+           "replay_matches_eager": replay_matches,
            "warm_us_per_step": warm * 1e6, "warm_gbs": case.kv_bytes / warm / 1e9,
            "partition_us_mean": mean_part * 1e3,
            "merge_us_mean": mean_merge * 1e3,
@@ -410,6 +435,28 @@ def traffic_for(workload: str, policy: str):
     return rec.get("bytes_per_launch"), (None if avg is None else round(avg * 1e-3, 3))
 
 
+def roofline_of(res: dict, probe=None) -> dict:
+    """Roofline object of one timed workload/policy: the partition kernel's
+    algorithmic K+V bytes / its mean launch duration, against the 8 TB/s peak,
+    with the rocprofv3 mean duration, calibrated HBM traffic and busy figures
+    recorded in profiles/ for the same kernel source (null when none)."""
+    rec = traffic_record(res["workload"], res["policy"])
+    achieved = res["partition_gbs"]
+    avg = rec.get("partition_avg_ns")
+    out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / PEAK_GBS, 4), "traffic": rec.get("bytes_per_launch"),
+           "kernel": "partition_kernel", "kernel_us_mean": round(res["partition_us_mean"], 3),
+           "kernel_us_rocprof": None if avg is None else round(avg * 1e-3, 3),
+           "valu_busy_pct": _round(rec.get("valu_busy_pct")),
+           "mfma_util_pct": _round(rec.get("mfma_util_pct")),
+           "merge_us_mean": round(res["merge_us_mean"], 3)}
+    if probe:
+        out["frac_of_read_probe"] = round(achieved / probe["gbs"], 4)
+        same = probe["same_size"].get(res["workload"])
+        out["frac_of_read_probe_same_size"] = round(achieved / same["gbs"], 4) if same else None
+    return out
+
+
 # ---------------------------------------------------------------- rocprof --
 
 def _rocpd(path: str, pattern: str):
@@ -525,7 +572,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     case = bench_case(args.workload)
     head = time_workload(case, args.policy, args.steps, args.warmup)
-    print(f"[bench] {case.name}/{args.policy}: {head['us_per_step']:.1f} us/step wall, "
+    print(f"[bench] {case.name}/{args.policy}: {head['us_per_step']:.1f} us/step, "
           f"{head['gbs']:.0f} GB/s, partition {head['partition_us_mean']:.1f} us", file=sys.stderr,
           flush=True)
 
@@ -549,9 +596,8 @@ def main():
                 if (pol == "fused" and name not in FUSED_ROWS) or (pol == "valu" and name not in VALU_ROWS):
                     continue
                 r = time_workload(c, pol, args.steps, args.warmup)
-                also[f"{name}/{pol}"] = {k: (round(v, 3) if isinstance(v, float) else v)
-                                         for k, v in r.items() if k not in ("workload", "policy")}
-                print(f"[bench] {name}/{pol}: {r['us_per_step']:.1f} us/step wall, {r['gbs']:.0f} GB/s, "
+                also[f"{name}/{pol}"] = r
+                print(f"[bench] {name}/{pol}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s, "
                       f"partition {r['partition_us_mean']:.1f} us ({r['partition_gbs']:.0f} GB/s)",
                       file=sys.stderr, flush=True)
 
@@ -560,8 +606,12 @@ def main():
         if k.endswith("/default") and not k.startswith("tiny_") and XSPLIT_SUFFIX not in k:
             sizes[k.split("/")[0]] = r["kv_bytes"]
     probe = None if args.no_also else read_probe(sizes=sizes)
-    achieved = head["partition_gbs"]
-    traffic, rocprof_us = traffic_for(case.name, args.policy)
+    also_out = {}
+    for key, r in also.items():
+        rec = {k: (round(v, 3) if isinstance(v, float) else v)
+               for k, v in r.items() if k not in ("workload", "policy")}
+        rec["roofline"] = roofline_of(r, probe)
+        also_out[key] = rec
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -580,11 +630,15 @@ def main():
                    "v1_max_ctx": head["v1_max_ctx"], "kv_bytes": case.kv_bytes,
                    "kv_copies_rotated": head["copies"]},
         "us_per_step": round(head["us_per_step"], 2),
-        "pct_of_peak": round(head["pct_of_peak"], 2),
-        "timing": "graph replay of the timed steps between synchronisations (wall clock); "
-                  "kernel times: HIP events around the steps' partition (then merge) "
-                  "launches issued back to back; step_us_events: events around each "
-                  "eager step, dispatch included",
+        "pct_of_peak": round(100.0 * head["gbs"] / PEAK_GBS, 2),
+        "timing": "graph replay of the timed steps between synchronisations; a bounded spin "
+                  "kernel ahead of the replay, and HIP events on the launch stream around it "
+                  "(wall_us_per_step: the same replay timed by the host clock with no spin); "
+                  "kernel times: HIP events around the steps' partition (then merge) launches "
+                  "issued back to back; step_us_events: events around each eager step, "
+                  "dispatch included",
+        "replay_matches_eager": head["replay_matches_eager"],
+        "wall_us_per_step": round(head["wall_us_per_step"], 2),
         "warm": {"us_per_step": round(head["warm_us_per_step"], 2),
                  "gbs": round(head["warm_gbs"], 1),
                  "note": "unflushed: every step reads the same K/V copy, so the 256 MB "
@@ -592,21 +646,10 @@ def main():
         "step_us_events": {"median": round(head["step_us_events_median"], 2),
                            "p10": round(head["step_us_events_p10"], 2),
                            "p90": round(head["step_us_events_p90"], 2)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "partition_kernel",
-                     "kernel_us_mean": round(head["partition_us_mean"], 3),
-                     "kernel_us_rocprof": rocprof_us,
-                     "valu_busy_pct": _round(traffic_record(case.name, args.policy).get("valu_busy_pct")),
-                     "mfma_util_pct": _round(traffic_record(case.name, args.policy).get("mfma_util_pct")),
-                     "merge_us_mean": round(head["merge_us_mean"], 3),
-                     "frac_of_read_probe": (round(achieved / probe["gbs"], 4) if probe else None),
-                     "frac_of_read_probe_same_size": (
-                         round(achieved / probe["same_size"][case.name]["gbs"], 4)
-                         if probe and case.name in probe["same_size"] else None)},
+        "roofline": roofline_of(head, probe),
         "read_probe": probe,
         "cpu_baseline": cpu,
-        "also": also,
+        "also": also_out,
         "kernel_source_sha": source_hash(),
     }
     print(json.dumps(line), flush=True)
