@@ -139,7 +139,7 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
         else:
             call = gq.prepare(q, k0, v0, scale=case.scale, policy=pol, stream=stream)
         max_ctx = case.max_blocks * case.block_size if case.block_table is not None else case.s_kv
-        has_merge = gq.workspace_size(case.num_seqs, case.h_q, case.h_kv, case.d, max_ctx, pol) > 0
+        has_merge = max_ctx > pol.v1_max_ctx          # some sequence may split
 
         for i in range(warmup):
             call(ks[i % copies], vs[i % copies], phases=3)

@@ -126,6 +126,10 @@ struct Params {
   float* part_o;                // partial un-normalised O row per (slot, query head)
   int4* desc;                   // balanced mode, paged: per (sequence, head group) segment record
   int* cnt;                     // fused merge: segments finished per (sequence, head group)
+  int* fixed_hdr;               // fixed mode, paged: [0] items listed
+  int2* items;                  // fixed mode, paged: (s * h_kv + j0, 4 p + log2 heads), largest first
+  int plan_shift;               // fixed mode, paged: size class = tiles * heads >> plan_shift
+  int hpw2;                     // fixed mode, paged: KV heads per item of a split sequence
   int num_seqs;
   int h_q;
   int h_kv;
@@ -910,39 +914,132 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
   }
 }
 
-// ------------------------------------------------- fixed-partition kernel --
+// ------------------------------------------- fixed-partition decomposition --
 //
-// One workgroup per (partition p, head group, sequence s), one wave per KV
-// head of the group; the kernel-map page's decomposition: a sequence of at
-// most v1_max_ctx tokens is one partition written directly, a longer one is
-// cut into ceil(L / part_size) partitions whose partials land at [s, i, p].
-// NT selects non-temporal K/V loads.  They raise the read rate when many
-// workgroups stream at once, but a lone wave that walks a whole long sequence
-// is latency-bound and runs faster with ordinary loads (the host decides).
-// SPLIT: a workgroup of one or two KV heads gives each head wph waves, which
-// split the partition's tiles (as in the balanced kernel).
+// The kernel-map page's decomposition: a sequence of at most v1_max_ctx
+// tokens is one partition written directly ("paged_attention_v1"); a longer
+// one is cut into ceil(L / part_size) partitions whose partials land at
+// [s, i, p] ("paged_attention_v2").  A work item is one partition of a group
+// of KV heads.
+//
+// Contiguous cache: every sequence has the same length, so the items are
+// equal and the host knows their number; one workgroup per item.
+//
+// Paged cache: the planner kernel (one workgroup) lists the items in the
+// workspace longest first, by a counting sort over their size (tokens times
+// heads), and the partition kernel takes item b, b + grid, ... in list order
+// (a grid of at most kFixedGridCap workgroups, no larger than the items can
+// be), so the hardware dispatcher starts the longest items first and hands
+// each CU the next item as it frees up.  Single-pass items take the host's
+// head group (narrow, so that they are many and balance well); partitions of
+// split sequences take groups of up to four heads (wide: a partition is
+// short).  A workgroup has the waves of max_heads_per_group(d); the waves of
+// an item's head split its tiles and merge in LDS (as in the balanced
+// kernel), so a single-pass item stays single-pass.  Which workgroup computes
+// an item changes nothing in its result.
 
+constexpr int kPlanBuckets = 256;                 // size classes of the planner's sort
+constexpr int kPlanThreads = 1024;
+
+// Items of a sequence of L tokens: partitions, heads per item, and size class
+// (bucket 0 holds the largest items).
+__device__ __forceinline__ void fixed_items(const Params& a, int L, int* n_part, int* heads,
+                                            int* bucket) {
+  const bool split = L > a.v1_max_ctx;
+  *n_part = split ? (L + a.part_size - 1) / a.part_size : 1;
+  *heads = split ? a.hpw2 : a.hpw;
+  const int tiles = split ? (a.part_size + kTile - 1) / kTile : (L + kTile - 1) / kTile;
+  *bucket = (kPlanBuckets - 1) - min(kPlanBuckets - 1, (tiles * *heads) >> a.plan_shift);
+}
+
+__device__ __forceinline__ int log2_heads(int h) { return h >= 4 ? 2 : h >= 2 ? 1 : 0; }
+
+__global__ __launch_bounds__(kPlanThreads) void fixed_plan_kernel(Params a) {
+  __shared__ int start[kPlanBuckets];             // items before bucket b (after the scan)
+  __shared__ int fill[kPlanBuckets];              // items placed in bucket b so far
+  __shared__ int wave_sum[kPlanBuckets / 64];
+  for (int b = threadIdx.x; b < kPlanBuckets; b += blockDim.x) start[b] = fill[b] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+    int np, nh, b;
+    fixed_items(a, seq_len<true>(a, s), &np, &nh, &b);
+    atomicAdd(&start[b], np * (a.h_kv / nh));
+  }
+  __syncthreads();
+  // exclusive scan of the bucket counts: a shuffle scan per wave of 64 buckets
+  const int lane = threadIdx.x & 63;
+  int v = 0, incl = 0;
+  if (threadIdx.x < kPlanBuckets) {
+    v = incl = start[threadIdx.x];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) wave_sum[threadIdx.x >> 6] = incl;
+  }
+  __syncthreads();
+  if (threadIdx.x < kPlanBuckets) {
+    int before = 0;
+    for (int u = 0; u < (int)(threadIdx.x >> 6); ++u) before += wave_sum[u];
+    start[threadIdx.x] = before + incl - v;
+    if (threadIdx.x == kPlanBuckets - 1) a.fixed_hdr[0] = before + incl;   // items listed
+  }
+  __syncthreads();
+  // item (s * h_kv + first KV head, 4 p + log2 heads)
+  for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x) {
+    int np, nh, b;
+    fixed_items(a, seq_len<true>(a, s), &np, &nh, &b);
+    const int ng = a.h_kv / nh;
+    int at = start[b] + atomicAdd(&fill[b], np * ng);
+    for (int p = 0; p < np; ++p)
+      for (int g = 0; g < ng; ++g)
+        a.items[at++] = make_int2(s * a.h_kv + g * nh, 4 * p + log2_heads(nh));
+  }
+}
+
+// One workgroup per item (contiguous) or items blockIdx.x, blockIdx.x + grid,
+// ... of the planner's list (paged).  NT selects non-temporal K/V loads: they
+// raise the read rate when many workgroups stream at once, but a lone wave
+// that walks a whole long sequence is latency-bound and runs faster with
+// ordinary loads (the host decides; paged items always split over waves).
 template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_kernel(Params a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
   __shared__ float2 mlx[SPLIT ? kMaxHeadsPerGroup * 16 : 1];         // sub-wave (m, l) exchange
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p = blockIdx.x % a.max_parts;
-  const int rest = blockIdx.x / a.max_parts;
-  const int hg = rest % a.n_groups;
-  const int s = rest / a.n_groups;
-  const int L = seq_len<PAGED>(a, s);
-  const bool split = L > a.v1_max_ctx;
-  const int n_part = split ? (L + a.part_size - 1) / a.part_size : 1;
-  if (p >= n_part) return;                       // uniform over the workgroup
-  const int t0 = split ? p * a.part_size : 0;
-  const int t1 = split ? min(t0 + a.part_size, L) : L;
-  const int j = hg * a.hpw + (SPLIT ? w % a.hpw : w);
-  const int64_t row0 = ((int64_t)s * a.h_kv + j) * a.ncol;   // partial rows per (s, j, column)
-  wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
-      a, smem, smem + ((XS && !SPLIT) ? 0 : w * Geo<D>::V_TILE), mlx, s, j, t0, t1, !split,
-      a.part_ml + row0 * a.max_parts + p, a.max_parts, a.part_o + (row0 * a.max_parts + p) * D,
-      (int64_t)a.max_parts * D);
+  auto item = [&](const Params& b, int s, int j, int p) {
+    const int L = seq_len<PAGED>(b, s);
+    const bool split = L > b.v1_max_ctx;
+    const int t0 = split ? p * b.part_size : 0;
+    const int t1 = split ? min(t0 + b.part_size, L) : L;
+    const int64_t row0 = ((int64_t)s * b.h_kv + j) * b.ncol;   // partial rows per (s, j, column)
+    wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
+        b, smem, smem + ((XS && !SPLIT) ? 0 : w * Geo<D>::V_TILE), mlx, s, j, t0, t1, !split,
+        b.part_ml + row0 * b.max_parts + p, b.max_parts, b.part_o + (row0 * b.max_parts + p) * D,
+        (int64_t)b.max_parts * D);
+  };
+  if constexpr (PAGED) {
+    static_assert(SPLIT, "paged items split their tiles over the workgroup's waves");
+    const int waves = blockDim.x >> 6;
+    const int n_items = a.fixed_hdr[0];
+    for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
+      const int2 it = a.items[idx];
+      const int s = __builtin_amdgcn_readfirstlane(it.x) / a.h_kv;
+      const int j0 = __builtin_amdgcn_readfirstlane(it.x) - s * a.h_kv;
+      const int code = __builtin_amdgcn_readfirstlane(it.y);
+      Params b = a;
+      b.hpw = 1 << (code & 3);                     // heads of this item
+      b.wph = waves >> (code & 3);                 // waves per head
+      item(b, s, j0 + w % b.hpw, code >> 2);
+    }
+  } else {
+    const int p = blockIdx.x % a.max_parts;
+    const int rest = blockIdx.x / a.max_parts;
+    const int hg = rest % a.n_groups;
+    const int s = rest / a.n_groups;
+    item(a, s, hg * a.hpw + (SPLIT ? w % a.hpw : w), p);
+  }
 }
 
 // --------------------------------------------------------- fused merge --
@@ -1381,9 +1478,15 @@ gqa_status_t scratch_address(void** out) {
 
 constexpr int32_t kDefaultV1Max = 256;
 constexpr int32_t kFallbackPartition = 512;
-// Fixed partitions: fewest work items (partition, head group, sequence) before
-// head groups are narrowed: one per CU of an MI355X.
+// Fixed partitions: fewest work items (partition, head group, sequence) the
+// host can count before it narrows the head groups: one per CU of an MI355X
+// for a contiguous cache (equal items), four for a paged one (single-pass items
+// of unknown lengths, which balance only when there are many).
 constexpr int64_t kFixedMinItems = 256;
+constexpr int64_t kFixedMinItemsPaged = 1024;
+// Workgroups of a paged fixed-partition launch, at most: items beyond the grid
+// are taken in further rounds.
+constexpr int64_t kFixedGridCap = 2048;
 
 struct Problem {
   bool paged;
@@ -1457,7 +1560,9 @@ struct Plan {
   bool can_split;     // some sequence may exceed v1_max_ctx
   bool fused;         // split ranges merged by their last workgroup (no merge kernel)
   int vc;             // vector-ALU products with vc columns (4 or 8); 0: matrix cores
-  size_t ws_desc, ws_cnt, ws_ml, ws_o, ws_total;   // byte sizes of the workspace regions
+  bool paged;         // paged cache (the fixed decomposition then plans a work list)
+  int hpw2;           // fixed, paged: KV heads per item of a split sequence
+  size_t ws_desc, ws_cnt, ws_hdr, ws_items, ws_ml, ws_o, ws_total;   // workspace region bytes
 };
 
 int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
@@ -1465,39 +1570,54 @@ int64_t upper_tiles(int num_seqs, int n_groups, int max_ctx) {
 }
 
 // Byte sizes of the workspace regions.  The balanced decomposition gives each
-// of its (at most grid_rows) workgroups two partial slots; the fixed one a
-// slot per (sequence, query row, partition).
+// of its (at most grid_rows) workgroups two partial slots, plus a record per
+// (sequence, head group); the fixed one has, for a paged cache, its work list
+// (a header and up to one item per (sequence, KV head, partition)) and, when a
+// sequence can be split, a partial slot per (sequence, query row, partition).
 void size_workspace(Plan& pl, int num_seqs, int t_q, int h_q, int h_kv, int d, int64_t grid_rows) {
+  pl.ws_desc = pl.ws_cnt = pl.ws_hdr = pl.ws_items = pl.ws_ml = pl.ws_o = 0;
   if (pl.balanced) {
-    const size_t rows = (size_t)2 * grid_rows * pl.hpw * (h_q / h_kv) * t_q;
-    pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
-    pl.ws_cnt = pl.fused ? align256((size_t)num_seqs * pl.n_groups * sizeof(int)) : 0;
-    pl.ws_ml = align256(rows * sizeof(float2));
-    pl.ws_o = rows * (size_t)d * sizeof(float);
+    if (pl.can_split) {
+      const size_t rows = (size_t)2 * grid_rows * pl.hpw * (h_q / h_kv) * t_q;
+      pl.ws_desc = align256((size_t)num_seqs * pl.n_groups * sizeof(int4));
+      pl.ws_cnt = pl.fused ? align256((size_t)num_seqs * pl.n_groups * sizeof(int)) : 0;
+      pl.ws_ml = align256(rows * sizeof(float2));
+      pl.ws_o = rows * (size_t)d * sizeof(float);
+    }
   } else {
-    const size_t rows = (size_t)num_seqs * h_q * t_q * pl.max_parts;
-    pl.ws_desc = 0;
-    pl.ws_cnt = 0;
-    pl.ws_ml = align256(rows * sizeof(float2));
-    pl.ws_o = rows * (size_t)d * sizeof(float);
+    if (pl.paged) {
+      pl.ws_hdr = 256;
+      pl.ws_items =
+          align256((size_t)num_seqs * h_kv * (pl.can_split ? pl.max_parts : 1) * sizeof(int2));
+    }
+    if (pl.can_split) {
+      const size_t rows = (size_t)num_seqs * h_q * t_q * pl.max_parts;
+      pl.ws_ml = align256(rows * sizeof(float2));
+      pl.ws_o = rows * (size_t)d * sizeof(float);
+    }
   }
-  pl.ws_total = pl.ws_desc + pl.ws_cnt + pl.ws_ml + pl.ws_o;
+  pl.ws_total = pl.ws_desc + pl.ws_cnt + pl.ws_hdr + pl.ws_items + pl.ws_ml + pl.ws_o;
 }
 
 // Points the Params' workspace regions into ws (laid out as size_workspace says).
 void place_workspace(Params& prm, const Plan& pl, char* ws) {
-  prm.desc = pl.ws_desc ? reinterpret_cast<int4*>(ws) : nullptr;
-  prm.cnt = pl.ws_cnt ? reinterpret_cast<int*>(ws + pl.ws_desc) : nullptr;
-  prm.part_ml = reinterpret_cast<float2*>(ws + pl.ws_desc + pl.ws_cnt);
-  prm.part_o = reinterpret_cast<float*>(ws + pl.ws_desc + pl.ws_cnt + pl.ws_ml);
+  size_t at = 0;
+  auto take = [&](size_t n) -> char* { char* p = n ? ws + at : nullptr; at += n; return p; };
+  prm.desc = reinterpret_cast<int4*>(take(pl.ws_desc));
+  prm.cnt = reinterpret_cast<int*>(take(pl.ws_cnt));
+  prm.fixed_hdr = reinterpret_cast<int*>(take(pl.ws_hdr));
+  prm.items = reinterpret_cast<int2*>(take(pl.ws_items));
+  prm.part_ml = reinterpret_cast<float2*>(take(pl.ws_ml));
+  prm.part_o = reinterpret_cast<float*>(take(pl.ws_o));
 }
 
 // parts_per_seq: partitions every sequence is known to have (1 unless a
 // contiguous cache is longer than v1_max_ctx); it only steers the head grouping
 // of the fixed scheduler, never the workspace size.
 Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
-               const gqa_policy_t& pol, int64_t parts_per_seq = 1) {
+               const gqa_policy_t& pol, bool paged, int64_t parts_per_seq = 1) {
   Plan pl{};
+  pl.paged = paged;
   pl.hpw = heads_per_group(h_kv, d);
   // a workgroup of fewer than the full complement of waves gives each KV head
   // several waves, which split its segments (more loads in flight per head)
@@ -1517,13 +1637,12 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
     pl.vc = (h_q / h_kv) * t_q <= 4 ? 4 : 8;
   pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
   pl.max_parts = pl.can_split ? (int)(((int64_t)max_ctx + pl.part_size - 1) / pl.part_size) : 1;
-  if (!pl.balanced) {
-    // A workgroup per (partition, head group, sequence).  With fewer work items
-    // than kFixedMinItems (e.g. 64 unsplit sequences in two groups of four KV
-    // heads: 128), narrow
-    // the head groups, down to one KV head per workgroup as the pages have it;
-    // a group of one or two heads gives each head several waves, which split
-    // its partition's tiles.
+  if (!pl.balanced && !paged) {
+    // One workgroup per (partition, head group, sequence).  With fewer work
+    // items than kFixedMinItems (e.g. 8 unsplit sequences in two groups of four
+    // KV heads: 16), narrow the head groups, down to one KV head per workgroup
+    // as the pages have it; a group of one or two heads gives each head several
+    // waves, which split its partition's tiles.
     while (pl.hpw > 1 && (int64_t)num_seqs * parts_per_seq * (h_kv / pl.hpw) < kFixedMinItems) {
       int h = pl.hpw - 1;
       while (h > 1 && h_kv % h != 0) --h;
@@ -1532,16 +1651,35 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
     pl.n_groups = h_kv / pl.hpw;
     // as in the balanced scheduler, only groups of one or two heads split
     if (pl.hpw <= 2) pl.wph = max_heads_per_group(d) / pl.hpw;
+  } else if (!pl.balanced) {
+    // Paged: items of 1, 2 or 4 heads, so that the workgroup's waves divide
+    // evenly among an item's heads.  Single-pass items narrow until the host
+    // can count kFixedMinItemsPaged of them (every sequence may be a single
+    // long pass, up to v1_max_ctx tokens); partitions of split sequences are
+    // short and take the widest group.
+    const int waves = max_heads_per_group(d);
+    auto pow2_group = [&](int cap) {
+      int h = 1;
+      while (2 * h <= std::min(cap, waves) && h_kv % (2 * h) == 0) h *= 2;
+      return h;
+    };
+    pl.hpw2 = pow2_group(kGroupHeads);
+    pl.hpw = pl.hpw2;
+    while (pl.hpw > 1 && (int64_t)num_seqs * (h_kv / pl.hpw) < kFixedMinItemsPaged) pl.hpw /= 2;
+    pl.n_groups = h_kv / pl.hpw;
+    pl.wph = waves / pl.hpw;
   }
-  if (!pl.can_split) return pl;
-  pl.fused = pl.balanced && (pol.flags & GQA_POLICY_FUSED_MERGE) != 0;
+  pl.fused = pl.balanced && pl.can_split && (pol.flags & GQA_POLICY_FUSED_MERGE) != 0;
   size_workspace(pl, num_seqs, t_q, h_q, h_kv, d, kMaxGrid);
   return pl;
 }
 
 // Resident workgroups for a kernel, cached per (device, kernel, block, dynamic
-// LDS); *cus_out receives the device's CU count.
-int resident_grid(const void* kernel, int block, size_t dyn_lds, int* cus_out = nullptr) {
+// LDS rounded up to 4 KB); *cus_out receives the device's CU count.  The
+// occupancy is queried for the rounded size, which never overstates it, so
+// calls whose LDS differs by a few sequences of prefix share one entry.
+int resident_grid(const void* kernel, int block, size_t dyn_lds_exact, int* cus_out = nullptr) {
+  const size_t dyn_lds = (dyn_lds_exact + 4095) & ~(size_t)4095;
   struct Entry { int dev; const void* k; int block; size_t lds; int grid; int cus; };
   static std::mutex mu;
   static Entry cache[64];
@@ -1596,6 +1734,17 @@ size_t balanced_lds(const Params& prm, const Plan& pl) {
          (PAGED ? (size_t)(prm.num_seqs + 1) * sizeof(int32_t) : 0);
 }
 
+// Workgroups of a persistent launch of `waves`-wave workgroups: enough for
+// kWavesPerCu waves on every CU (one workgroup per CU when it has that many
+// waves), at most as many as fit at once.  0 if the device cannot be queried.
+int persistent_grid(const void* kern, int waves, size_t dyn_lds) {
+  int cus = 0;
+  const int resident = resident_grid(kern, 64 * waves, dyn_lds, &cus);
+  if (resident <= 0) return 0;
+  const int per_cu = std::max(1, (kWavesPerCu + waves - 1) / waves);
+  return std::min(resident, std::max(1, cus) * per_cu);
+}
+
 // Workgroups of the balanced partition launch: enough for kWavesPerCu waves
 // on every CU (one workgroup per CU when it has that many waves), at most the
 // resident count and kMaxGrid, and no more than gives every workgroup
@@ -1604,13 +1753,9 @@ size_t balanced_lds(const Params& prm, const Plan& pl) {
 // sequences into more partials for the merge.
 template <class DT, int D, bool PAGED, bool XS>
 int balanced_grid(const Params& prm, const Plan& pl) {
-  const void* kern = balanced_kernel<DT, D, PAGED, XS>(pl);
-  int cus = 0;
-  const int waves = pl.hpw * pl.wph;
-  const int resident0 = resident_grid(kern, 64 * waves, balanced_lds<D, PAGED, XS>(prm, pl), &cus);
-  if (resident0 <= 0) return 0;
-  const int per_cu = std::max(1, (kWavesPerCu + waves - 1) / waves);
-  const int resident = std::min(resident0, std::max(1, cus) * per_cu);
+  const int resident = persistent_grid(balanced_kernel<DT, D, PAGED, XS>(pl), pl.hpw * pl.wph,
+                                       balanced_lds<D, PAGED, XS>(prm, pl));
+  if (resident <= 0) return 0;
   const int64_t want =
       (upper_tiles(prm.num_seqs, pl.n_groups, prm.max_ctx) + kMinChunkTiles - 1) / kMinChunkTiles;
   return (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kMaxGrid, resident, want}));
@@ -1643,7 +1788,7 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
     grid_b = balanced_grid<DT, D, PAGED, XS>(prm, pl);
     if (grid_b <= 0) return GQA_ERR_LAUNCH;
   }
-  if (scratch && pl.can_split) {
+  if (scratch && pl.ws_total > 0) {
     Plan sized = pl;
     if (pl.balanced)
       size_workspace(sized, prm.num_seqs, prm.tq, prm.h_q, prm.h_kv, D, grid_b);
@@ -1671,20 +1816,32 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       if (hipLaunchKernel(kern, dim3(grid_b), dim3(block), args,
                           balanced_lds<D, PAGED, XS>(prm, pl), stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
+    } else if constexpr (PAGED) {
+      // the work list, then items blockIdx.x, blockIdx.x + grid, ... of it
+      if (hipLaunchKernel(reinterpret_cast<const void*>(&fixed_plan_kernel), dim3(1),
+                          dim3(kPlanThreads), args, 0, stream) != hipSuccess)
+        return GQA_ERR_LAUNCH;
+      const int waves = max_heads_per_group(D);
+      const int64_t bound = (int64_t)prm.num_seqs * prm.h_kv * pl.max_parts;   // items, at most
+      const int grid = (int)std::min(bound, kFixedGridCap);
+      if (hipLaunchKernel(reinterpret_cast<const void*>(
+                              &partition_fixed_kernel<DT, D, true, XS, true, true>),
+                          dim3(grid), dim3(64 * waves), args,
+                          (size_t)waves * Geo<D>::V_TILE * sizeof(uint16_t), stream) != hipSuccess)
+        return GQA_ERR_LAUNCH;
     } else {
       const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;
       // Non-temporal loads unless some wave may walk more than one partition's
       // worth of tokens in a single pass (a sequence of up to v1_max_ctx tokens
-      // that is not split); a contiguous cache longer than v1_max_ctx splits
-      // every sequence.
-      const bool short_walks = prm.v1_max_ctx <= prm.part_size || (!PAGED && prm.s_kv > prm.v1_max_ctx);
+      // that is not split).
+      const bool short_walks = prm.v1_max_ctx <= prm.part_size || prm.s_kv > prm.v1_max_ctx;
       const bool sw = pl.wph > 1;
       const void* kern =
           short_walks
-              ? (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true, true>)
-                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, true, false>))
-              : (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false, true>)
-                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, PAGED, XS, false, false>));
+              ? (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, true, true>)
+                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, true, false>))
+              : (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, false, true>)
+                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, false, false>));
       if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(block), args, tiles_lds<D, XS>(pl),
                           stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
@@ -1772,9 +1929,10 @@ gqa_status_t run(const Problem& pb) {
       (!pb.paged && pol.partition_size > 0 && pb.s_kv > pol.v1_max_ctx)
           ? ((int64_t)pb.s_kv + pol.partition_size - 1) / pol.partition_size
           : 1;
-  const Plan pl = make_plan(pb.num_seqs, pb.tq, pb.h_q, pb.h_kv, pb.d, max_ctx, pol, parts_per_seq);
+  const Plan pl =
+      make_plan(pb.num_seqs, pb.tq, pb.h_q, pb.h_kv, pb.d, max_ctx, pol, pb.paged, parts_per_seq);
   if ((pol.flags & GQA_POLICY_VALU_DOT2) && !pl.balanced) return GQA_ERR_UNSUPPORTED;
-  if (!pl.balanced && (int64_t)pl.max_parts * pl.n_groups * pb.num_seqs > INT32_MAX)
+  if (!pl.balanced && (int64_t)pl.max_parts * pb.h_kv * pb.num_seqs > INT32_MAX)
     return GQA_ERR_BAD_SHAPE;
   if ((int64_t)pb.h_q * pb.tq * pb.num_seqs > INT32_MAX) return GQA_ERR_BAD_SHAPE;
   if (pb.num_seqs == 0) return GQA_OK;
@@ -1824,6 +1982,17 @@ gqa_status_t run(const Problem& pb) {
   // with no workspace nothing may split: the single-pass bound covers every sequence
   prm.v1_max_ctx = pl.can_split ? pol.v1_max_ctx : max_ctx;
   prm.max_parts = pl.max_parts;
+  // fixed mode, paged: size classes of the planner's sort, (item tiles x heads) >> plan_shift
+  prm.hpw2 = pl.hpw2;
+  if (!pl.balanced && pb.paged) {
+    const int64_t v1_tiles = ((int64_t)std::min(prm.v1_max_ctx, max_ctx) + kTile - 1) / kTile;
+    const int64_t part_tiles = ((int64_t)pl.part_size + kTile - 1) / kTile;
+    int64_t largest = std::max(v1_tiles * pl.hpw, part_tiles * pl.hpw2);
+    while (largest >= kPlanBuckets) {
+      largest >>= 1;
+      ++prm.plan_shift;
+    }
+  }
   prm.c = pb.scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(pb.stream);
   char* scr = nullptr;
@@ -1894,7 +2063,7 @@ size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, in
   if (resolve_policy(policy, &pol) != GQA_OK) return 0;
   if (num_seqs < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || d_head <= 0 || max_ctx < 0)
     return 0;
-  return make_plan(num_seqs, 1, h_q, h_kv, d_head, max_ctx, pol).ws_total;
+  return make_plan(num_seqs, 1, h_q, h_kv, d_head, max_ctx, pol, true).ws_total;
 }
 
 gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -2003,7 +2172,8 @@ size_t gqa_decode_ex_workspace_size(const gqa_decode_args_t* args) {
   else
     return 0;
   if (max_ctx < 0 || max_ctx > (1 << 30)) return 0;
-  return make_plan(x.num_seqs, x.t_q, x.h_q, x.h_kv, x.d_head, (int)max_ctx, pol).ws_total;
+  return make_plan(x.num_seqs, x.t_q, x.h_q, x.h_kv, x.d_head, (int)max_ctx, pol,
+                   x.layout != GQA_KV_CONTIGUOUS).ws_total;
 }
 
 const char* gqa_status_string(gqa_status_t status) {

@@ -54,10 +54,15 @@ def test_policies(gq):
 
 def test_workspace_size(gq):
     P = gq.policy_pages()
-    assert gq.workspace_size(4, 32, 8, 128, 8192, P) == 0       # nothing can split
+    # fixed partitions: a 256-byte header and a work list of up to one 8-byte item per
+    # (sequence, KV head, partition); partials only when a sequence can split
+    items = 4 * 8 * 1 * 8
+    assert gq.workspace_size(4, 32, 8, 128, 8192, P) == 256 + ((items + 255) // 256) * 256
     n = gq.workspace_size(4, 32, 8, 128, 8193, P)               # 17 partitions
     rows = 4 * 32 * 17
-    assert n == ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
+    items = 4 * 8 * 17 * 8
+    assert n == 256 + ((items + 255) // 256) * 256 + ((rows * 8 + 255) // 256) * 256 + \
+        rows * 128 * 4
     # balanced: a record per (sequence, head group of up to 4 KV heads) + two partial
     # slots per workgroup (2048 workgroups at most), each holding the group's query heads
     B = gq.policy_default()
@@ -206,7 +211,9 @@ def test_ex_workspace_size(gq):
         assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(a)) == want
         a = _ex(gq, t_q=t_q, max_blocks_per_seq=512, policy=ctypes.pointer(P))
         rows = 2 * t_q * 8 * (8192 // 512)                    # fixed: [s, t_q, h_q, part]
-        want = ((rows * 8 + 255) // 256) * 256 + rows * 128 * 4
+        items = 2 * 2 * (8192 // 512) * 8                     # (s, KV head, part), 8 B each
+        want = 256 + ((items + 255) // 256) * 256 + ((rows * 8 + 255) // 256) * 256 + \
+            rows * 128 * 4
         assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(a)) == want
     a = _ex(gq, t_q=1, layout=0, s_kv=4096, policy=ctypes.pointer(B))
     assert gq.lib.gqa_decode_ex_workspace_size(ctypes.byref(a)) == \
