@@ -72,7 +72,7 @@ __host__ __device__ constexpr int max_heads_per_group(int d) {
 constexpr int kMaxGrid = 2048;       // persistent grid cap (two partial slots per workgroup)
 constexpr int kMinChunkTiles = 2;    // smallest balanced share: 2 tiles = 64 tokens
 constexpr int kWavesPerCu = 4;       // balanced grid: waves per CU it aims for (see balanced_grid)
-constexpr int kMaxSeqsBalanced = 8192;
+constexpr int kMaxSeqsBalanced = 7168;   // its prefix shares LDS with two V tiles per wave
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- dtypes --
@@ -172,6 +172,9 @@ __device__ __forceinline__ int seq_len(const Params& a, int s) {
   }
 }
 
+// Cache-policy operand of global_load_lds for a non-temporal load (the nt bit).
+constexpr int kAuxNontemporal = 2;
+
 // K and V are read exactly once per call, so their loads are non-temporal:
 // they do not displace the partials, tables and queries the caches hold (on
 // MI355X this raises the partition kernel's read rate by about a tenth).
@@ -224,8 +227,22 @@ struct Geo {
   static constexpr int CH = D / 8;         // 16-byte chunks per K/V row
   static constexpr int RPI = 64 / CH;      // V rows per 16-byte load instruction
   static constexpr int NIT = kTile / RPI;  // V load instructions per tile
-  static constexpr int V_TILE = kTile * D; // uint16 per staged V tile (one per wave)
+  static constexpr int V_TILE = kTile * D; // uint16 per staged V tile
 };
+
+// With the row layouts the V tile goes from HBM straight into LDS (gfx950's
+// global_load_lds_dwordx4, which writes lane l's 16 bytes at the LDS base +
+// 16 l), double-buffered so that the next tile's V lands while the current
+// one is read; the matrix-core operand V^T is then read back with the
+// transposing LDS read ds_read_b64_tr_b16.  No V passes through registers.
+constexpr bool kVdma = true;
+
+// LDS of one wave of the matrix-core segment code, in uint16: its V tiles
+// (row layouts), or one tile for the sub-wave state exchange (x-split).
+template <int D, bool XS>
+__host__ __device__ constexpr int wave_lds_elems() {
+  return (!XS && kVdma ? 2 : 1) * Geo<D>::V_TILE;
+}
 
 // ------------------------------------------------- one wave, one segment --
 //
@@ -306,7 +323,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
 
   struct TileRows {
     uint4_t k[2][KK];
-    uint4_t v[NIT];
+    uint4_t v[kVdma ? 1 : NIT];                  // (kVdma: V goes to LDS, not registers)
   };
   struct TileX {
     uint4_t k[2][KK];
@@ -319,7 +336,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   // offsets.  Rows past t1 are clamped to the last live token of the segment,
   // so every load is in bounds and unconditional; those rows are masked
   // afterwards (score -inf, hence a zero weight on a finite V row).
-  auto load = [&](Tile& T, int tb) {
+  auto load = [&](Tile& T, int tb, uint16_t* vbuf) {
     const uint16_t* kb[2];
     const uint16_t* vb[2];
     int last[2];                                  // last live row of each half
@@ -375,8 +392,19 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
       for (int it = 0; it < NIT; ++it) {
         const int r = it * RPI + lane / CH;
         const int hb = r >> 4;                      // uniform per instruction
-        const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
-        T.v[it] = load_stream<uint4_t, NT>(vb[hb] + off);
+        if constexpr (kVdma) {
+          // lane l fills LDS position l % CH of row r, which holds chunk
+          // (l % CH) ^ swizzle(r) of the row (the staged layout below)
+          const int c = (lane % CH) ^ v_swizzle(r);
+          const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + c * 8;
+          __builtin_amdgcn_global_load_lds(
+              reinterpret_cast<const void*>(vb[hb] + off),
+              (__attribute__((address_space(3))) void*)(vbuf + it * 64 * 8), 16, 0,
+              NT ? kAuxNontemporal : 0);
+        } else {
+          const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
+          T.v[it] = load_stream<uint4_t, NT>(vb[hb] + off);
+        }
       }
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -389,14 +417,14 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   };
 
   // fold the tile starting at token tb into (m_run, l_run, acc)
-  auto compute = [&](const Tile& T, int tb) {
-    if constexpr (!XS) {
+  auto compute = [&](const Tile& T, int tb, const uint16_t* vbuf) {
+    if constexpr (!XS && !kVdma) {
       // stage V: row r, chunk c at position c ^ swizzle(r)
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int r = it * RPI + lane / CH;
         const int pos = (lane % CH) ^ v_swizzle(r);
-        *reinterpret_cast<uint4_t*>(vt + r * D + pos * 8) = T.v[it];
+        *reinterpret_cast<uint4_t*>(vt + r * D + pos * 8) = T.v[kVdma ? 0 : it];
       }
     }
     // scores S^T = K . Q^T
@@ -467,16 +495,35 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
       wave_lds_fence();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        uint32_t vv[4];
+        uint4_t vop;
+        if constexpr (kVdma) {
+          // ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+          // element i % 4 of the 8-byte loads of lanes 4 e + i / 4 (e = 0..3).
+          // Lane (col, grp) loads row slot_token(grp, col / 4) (then the same
+          // token + 16) at d = 16 nb + 4 (col % 4), so it receives
+          // V[slot_token(grp, e)][16 nb + col]: its V^T operand row.
+          const int d0 = 16 * nb + 4 * (col & 3);
+          const int r0 = slot_token(grp, col >> 2), r1 = r0 + 16;
+          typedef short short4_t __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
+              const_cast<uint16_t*>(vbuf) + r0 * D + (((d0 >> 3) ^ v_swizzle(r0)) << 3) + (d0 & 7)));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
+              const_cast<uint16_t*>(vbuf) + r1 * D + (((d0 >> 3) ^ v_swizzle(r1)) << 3) + (d0 & 7)));
+          const uint2_t l2 = __builtin_bit_cast(uint2_t, lo), h2 = __builtin_bit_cast(uint2_t, hi);
+          vop = uint4_t{l2.x, l2.y, h2.x, h2.y};
+        } else {
+          uint32_t vv[4];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int d = 16 * nb + col;
-          const int ra = slot_token(grp, 2 * e2), rb = slot_token(grp, 2 * e2 + 1);
-          const uint32_t lo = vt[ra * D + (((d >> 3) ^ v_swizzle(ra)) << 3) + (d & 7)];
-          const uint32_t hi = vt[rb * D + (((d >> 3) ^ v_swizzle(rb)) << 3) + (d & 7)];
-          vv[e2] = lo | (hi << 16);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int d = 16 * nb + col;
+            const int ra = slot_token(grp, 2 * e2), rb = slot_token(grp, 2 * e2 + 1);
+            const uint32_t lo = vbuf[ra * D + (((d >> 3) ^ v_swizzle(ra)) << 3) + (d & 7)];
+            const uint32_t hi = vbuf[rb * D + (((d >> 3) ^ v_swizzle(rb)) << 3) + (d & 7)];
+            vv[e2] = lo | (hi << 16);
+          }
+          vop = uint4_t{vv[0], vv[1], vv[2], vv[3]};
         }
-        const uint4_t vop{vv[0], vv[1], vv[2], vv[3]};
         acc[nb] *= alpha;
         acc[nb] = DT::mfma(vop, phi4, acc[nb]);
         acc[nb] = DT::mfma(vop, plo4, acc[nb]);
@@ -493,38 +540,47 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   //      overlaps.  The current tile has landed before the next one is issued,
   //      so a wave never has more than one tile of loads outstanding.
   int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
-  if constexpr (D > 128) {
-    // d = 256: one register tile (32 KB of K/V per wave).  A wave waits for
-    // each tile; the other waves of the CU keep 3 x 32 KB in flight meanwhile.
+  // V buffers: with kVdma (row layouts) tile A stages into vt and tile B into
+  // the wave's second tile; otherwise both stage through registers into vt
+  uint16_t* const vbA = vt;
+  uint16_t* const vbB = (!XS && kVdma) ? vt + Geo<D>::V_TILE : vt;
+  if constexpr (D > 128 && !(kVdma && !XS)) {
+    // d = 256 with V in registers: one register tile (32 KB of K/V per wave).
+    // A wave waits for each tile; the other waves of the CU keep 3 x 32 KB in
+    // flight meanwhile.
     Tile A;
     for (int tb = t0; n > 0; --n, tb += kTile) {
-      load(A, tb);
-      compute(A, tb);
+      load(A, tb, vbA);
+      compute(A, tb, vbA);
     }
   } else if (n > 0) {
     Tile A, B;
     int tb = t0;
-    load(A, tb);
+    load(A, tb, vbA);
     while (n >= 3) {
       wait_tile_loads();
-      load(B, tb + kTile);
+      load(B, tb + kTile, vbB);
       __builtin_amdgcn_sched_barrier(0);
-      compute(A, tb);
+      compute(A, tb, vbA);
       wait_tile_loads();
-      load(A, tb + 2 * kTile);
+      load(A, tb + 2 * kTile, vbA);
       __builtin_amdgcn_sched_barrier(0);
-      compute(B, tb + kTile);
+      compute(B, tb + kTile, vbB);
       tb += 2 * kTile;
       n -= 2;
     }
+    // (the LDS-staged V of the last tiles has landed only after a wait: the
+    // compiler tracks register operands, not the LDS the loads write)
     if (n == 2) {
       wait_tile_loads();
-      load(B, tb + kTile);
+      load(B, tb + kTile, vbB);
       __builtin_amdgcn_sched_barrier(0);
-      compute(A, tb);
-      compute(B, tb + kTile);
+      compute(A, tb, vbA);
+      wait_tile_loads();
+      compute(B, tb + kTile, vbB);
     } else {
-      compute(A, tb);
+      wait_tile_loads();
+      compute(A, tb, vbA);
     }
   }
 
@@ -549,7 +605,8 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
         const float m_new = fmaxf(m_run, o2.x);
         const float a1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         const float a2 = o2.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o2.x - m_new);
-        const float4_t* other = reinterpret_cast<const float4_t*>(smem + w2 * Geo<D>::V_TILE);
+        const float4_t* other =
+            reinterpret_cast<const float4_t*>(smem + w2 * wave_lds_elems<D, XS>());
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = acc[nb] * a1 + other[nb * 64 + lane] * a2;
         l_run = l_run * a1 + o2.y * a2;
@@ -1015,7 +1072,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
     const int t1 = split ? min(t0 + b.part_size, L) : L;
     const int64_t row0 = ((int64_t)s * b.h_kv + j) * b.ncol;   // partial rows per (s, j, column)
     wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
-        b, smem, smem + ((XS && !SPLIT) ? 0 : w * Geo<D>::V_TILE), mlx, s, j, t0, t1, !split,
+        b, smem, smem + ((XS && !SPLIT) ? 0 : w * wave_lds_elems<D, XS>()), mlx, s, j, t0, t1, !split,
         b.part_ml + row0 * b.max_parts + p, b.max_parts, b.part_o + (row0 * b.max_parts + p) * D,
         (int64_t)b.max_parts * D);
   };
@@ -1144,7 +1201,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   const int nw = blockDim.x >> 6;                // = hpw * wph
   // per-wave tiles: V staging (row layout) and the sub-wave state exchange;
   // the x-split layout with one wave per head needs neither
-  constexpr int tile_elems = VC > 0 ? dot2_wave_elems(VC) : (XS && !SPLIT) ? 0 : Geo<D>::V_TILE;
+  constexpr int tile_elems = VC > 0 ? dot2_wave_elems(VC) : (XS && !SPLIT) ? 0 : wave_lds_elems<D, XS>();
   uint16_t* const vt = smem + w * tile_elems;
   int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * tile_elems);
 
@@ -1710,7 +1767,8 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds_exact, int* cus_
 template <int D, bool XS>
 size_t tiles_lds(const Plan& pl) {
   if (pl.vc > 0) return (size_t)pl.hpw * dot2_wave_elems(pl.vc) * sizeof(uint16_t);
-  return (XS && pl.wph == 1) ? 0 : (size_t)pl.hpw * pl.wph * Geo<D>::V_TILE * sizeof(uint16_t);
+  return (XS && pl.wph == 1) ? 0
+                             : (size_t)pl.hpw * pl.wph * wave_lds_elems<D, XS>() * sizeof(uint16_t);
 }
 
 template <class DT, int D, bool PAGED, bool XS>
@@ -1827,7 +1885,7 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       if (hipLaunchKernel(reinterpret_cast<const void*>(
                               &partition_fixed_kernel<DT, D, true, XS, true, true>),
                           dim3(grid), dim3(64 * waves), args,
-                          (size_t)waves * Geo<D>::V_TILE * sizeof(uint16_t), stream) != hipSuccess)
+                          (size_t)waves * wave_lds_elems<D, XS>() * sizeof(uint16_t), stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     } else {
       const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;

@@ -102,7 +102,7 @@ typedef enum gqa_status {
  * both, 1 = partition kernel only, 2 = merge kernel only (the merge then reads
  * the partials a phase-1 call with the same arguments left in the
  * workspace); it exists so that a caller can time the two kernels apart.
- * The balanced decomposition needs num_seqs <= 8192; a larger batch uses the
+ * The balanced decomposition needs num_seqs <= 7168; a larger batch uses the
  * fixed one with 512-token partitions.
  *
  * flags: 0, GQA_POLICY_FUSED_MERGE or GQA_POLICY_VALU_DOT2 (each for the

@@ -228,6 +228,21 @@ def test_head_groups(gq, h_kv, G, d):
         assert_close(got, ref, W.BF16, what=f"h_kv={h_kv} G={G} d={d} {name}")
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_most_sequences_balanced(gq, d):
+    """The largest batch the balanced scheduler takes (7168 sequences, whose prefix
+    shares the workgroup's LDS with its V tiles), one KV head, so that each head
+    gets several waves: mostly short sequences and a few long, split ones."""
+    rng = np.random.default_rng(7 + d)
+    lens = rng.integers(0, 48, size=7168).astype(np.int32)
+    lens[[5, 3000, 7167]] = [2500, 40000, 700]
+    case = W.paged_case(f"most{d}", 1310 + d, lens, h_q=8, h_kv=1, d=d, dtype=W.BF16)
+    heads = [(s, i) for s in list(range(0, 7168, 211)) + [5, 3000, 7167] for i in (0, 7)]
+    ref = R.decode(case, heads=heads)
+    got = run_case(case_to_device(case, DEV))
+    assert_close(got, ref, W.BF16, what=f"7168 sequences d={d}")
+
+
 def test_many_sequences_fallback(gq):
     """More sequences than the balanced scheduler keeps in LDS: fixed 512-token partitions."""
     rng = np.random.default_rng(5)
