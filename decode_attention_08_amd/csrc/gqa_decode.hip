@@ -990,10 +990,10 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
 // each CU the next item as it frees up.  Single-pass items take the host's
 // head group (narrow, so that they are many and balance well); partitions of
 // split sequences take groups of up to four heads (wide: a partition is
-// short).  A workgroup has the waves of max_heads_per_group(d); the waves of
-// an item's head split its tiles and merge in LDS (as in the balanced
-// kernel), so a single-pass item stays single-pass.  Which workgroup computes
-// an item changes nothing in its result.
+// short).  A workgroup has four waves; the waves of an item's head split its
+// tiles and merge in LDS (as in the balanced kernel), so a single-pass item
+// stays single-pass.  Which workgroup computes an item changes nothing in its
+// result.
 
 constexpr int kPlanBuckets = 256;                 // size classes of the planner's sort
 constexpr int kPlanThreads = 1024;
@@ -1055,47 +1055,62 @@ __global__ __launch_bounds__(kPlanThreads) void fixed_plan_kernel(Params a) {
   }
 }
 
-// One workgroup per item (contiguous) or items blockIdx.x, blockIdx.x + grid,
-// ... of the planner's list (paged).  NT selects non-temporal K/V loads: they
-// raise the read rate when many workgroups stream at once, but a lone wave
-// that walks a whole long sequence is latency-bound and runs faster with
-// ordinary loads (the host decides; paged items always split over waves).
+// One item: partition p of sequence s for KV head j (this wave's head).
 template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
+__device__ __forceinline__ void fixed_item(const Params& b, uint16_t* smem, float2* mlx, int w,
+                                           int s, int j, int p) {
+  const int L = seq_len<PAGED>(b, s);
+  const bool split = L > b.v1_max_ctx;
+  const int t0 = split ? p * b.part_size : 0;
+  const int t1 = split ? min(t0 + b.part_size, L) : L;
+  const int64_t row0 = ((int64_t)s * b.h_kv + j) * b.ncol;   // partial rows per (s, j, column)
+  wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
+      b, smem, smem + ((XS && !SPLIT) ? 0 : w * wave_lds_elems<D, XS>()), mlx, s, j, t0, t1, !split,
+      b.part_ml + row0 * b.max_parts + p, b.max_parts, b.part_o + (row0 * b.max_parts + p) * D,
+      (int64_t)b.max_parts * D);
+}
+
+// Contiguous cache: one workgroup per item.  NT selects non-temporal K/V
+// loads: they raise the read rate when many workgroups stream at once, but a
+// lone wave that walks a whole long sequence is latency-bound and runs faster
+// with ordinary loads (the host decides).  SPLIT: a group of one or two KV
+// heads gives each head several waves, which split the item's tiles.
+template <class DT, int D, bool XS, bool NT, bool SPLIT>
 __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_kernel(Params a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // one V tile per wave
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles per wave
   __shared__ float2 mlx[SPLIT ? kMaxHeadsPerGroup * 16 : 1];         // sub-wave (m, l) exchange
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  auto item = [&](const Params& b, int s, int j, int p) {
-    const int L = seq_len<PAGED>(b, s);
-    const bool split = L > b.v1_max_ctx;
-    const int t0 = split ? p * b.part_size : 0;
-    const int t1 = split ? min(t0 + b.part_size, L) : L;
-    const int64_t row0 = ((int64_t)s * b.h_kv + j) * b.ncol;   // partial rows per (s, j, column)
-    wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
-        b, smem, smem + ((XS && !SPLIT) ? 0 : w * wave_lds_elems<D, XS>()), mlx, s, j, t0, t1, !split,
-        b.part_ml + row0 * b.max_parts + p, b.max_parts, b.part_o + (row0 * b.max_parts + p) * D,
-        (int64_t)b.max_parts * D);
-  };
-  if constexpr (PAGED) {
-    static_assert(SPLIT, "paged items split their tiles over the workgroup's waves");
-    const int waves = blockDim.x >> 6;
-    const int n_items = a.fixed_hdr[0];
-    for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
-      const int2 it = a.items[idx];
-      const int s = __builtin_amdgcn_readfirstlane(it.x) / a.h_kv;
-      const int j0 = __builtin_amdgcn_readfirstlane(it.x) - s * a.h_kv;
-      const int code = __builtin_amdgcn_readfirstlane(it.y);
-      Params b = a;
-      b.hpw = 1 << (code & 3);                     // heads of this item
-      b.wph = waves >> (code & 3);                 // waves per head
-      item(b, s, j0 + w % b.hpw, code >> 2);
-    }
-  } else {
-    const int p = blockIdx.x % a.max_parts;
-    const int rest = blockIdx.x / a.max_parts;
-    const int hg = rest % a.n_groups;
-    const int s = rest / a.n_groups;
-    item(a, s, hg * a.hpw + (SPLIT ? w % a.hpw : w), p);
+  const int p = blockIdx.x % a.max_parts;
+  const int rest = blockIdx.x / a.max_parts;
+  const int hg = rest % a.n_groups;
+  const int s = rest / a.n_groups;
+  fixed_item<DT, D, false, XS, NT, SPLIT>(a, smem, mlx, w, s, hg * a.hpw + (SPLIT ? w % a.hpw : w), p);
+}
+
+// Paged cache: items blockIdx.x, blockIdx.x + grid, ... of the planner's list.
+// A workgroup has kFixedPagedWaves waves and runs alone on its CU: its LDS
+// request is at least kFixedPagedLds, more than half of the CU's 160 KB.  On
+// MI355X four waves per CU, each with one tile of loads in flight, stream
+// faster than eight.  The waves of an item's head split its tiles and merge in
+// LDS.
+constexpr int kFixedPagedWaves = 4;
+constexpr size_t kFixedPagedLds = 96 * 1024;
+
+template <class DT, int D, bool XS>
+__global__ __launch_bounds__(kFixedPagedWaves * 64) void partition_fixed_paged_kernel(Params a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles per wave
+  __shared__ float2 mlx[kFixedPagedWaves * 16];                      // sub-wave (m, l) exchange
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_items = a.fixed_hdr[0];
+  for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
+    const int2 it = a.items[idx];
+    const int s = __builtin_amdgcn_readfirstlane(it.x) / a.h_kv;
+    const int j0 = __builtin_amdgcn_readfirstlane(it.x) - s * a.h_kv;
+    const int code = __builtin_amdgcn_readfirstlane(it.y);
+    Params b = a;
+    b.hpw = 1 << (code & 3);                       // heads of this item
+    b.wph = kFixedPagedWaves >> (code & 3);        // waves per head
+    fixed_item<DT, D, true, XS, true, true>(b, smem, mlx, w, s, j0 + w % b.hpw, code >> 2);
   }
 }
 
@@ -1714,7 +1729,7 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
     // can count kFixedMinItemsPaged of them (every sequence may be a single
     // long pass, up to v1_max_ctx tokens); partitions of split sequences are
     // short and take the widest group.
-    const int waves = max_heads_per_group(d);
+    const int waves = kFixedPagedWaves;
     auto pow2_group = [&](int cap) {
       int h = 1;
       while (2 * h <= std::min(cap, waves) && h_kv % (2 * h) == 0) h *= 2;
@@ -1879,13 +1894,13 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       if (hipLaunchKernel(reinterpret_cast<const void*>(&fixed_plan_kernel), dim3(1),
                           dim3(kPlanThreads), args, 0, stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
-      const int waves = max_heads_per_group(D);
       const int64_t bound = (int64_t)prm.num_seqs * prm.h_kv * pl.max_parts;   // items, at most
       const int grid = (int)std::min(bound, kFixedGridCap);
-      if (hipLaunchKernel(reinterpret_cast<const void*>(
-                              &partition_fixed_kernel<DT, D, true, XS, true, true>),
-                          dim3(grid), dim3(64 * waves), args,
-                          (size_t)waves * wave_lds_elems<D, XS>() * sizeof(uint16_t), stream) != hipSuccess)
+      if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_fixed_paged_kernel<DT, D, XS>),
+                          dim3(grid), dim3(64 * kFixedPagedWaves), args,
+                          std::max(kFixedPagedLds, (size_t)kFixedPagedWaves *
+                                                       wave_lds_elems<D, XS>() * sizeof(uint16_t)),
+                          stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     } else {
       const int64_t grid = (int64_t)pl.max_parts * pl.n_groups * prm.num_seqs;
@@ -1896,10 +1911,10 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       const bool sw = pl.wph > 1;
       const void* kern =
           short_walks
-              ? (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, true, true>)
-                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, true, false>))
-              : (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, false, true>)
-                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, false, XS, false, false>));
+              ? (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, XS, true, true>)
+                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, XS, true, false>))
+              : (sw ? reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, XS, false, true>)
+                    : reinterpret_cast<const void*>(&partition_fixed_kernel<DT, D, XS, false, false>));
       if (hipLaunchKernel(kern, dim3((unsigned)grid), dim3(block), args, tiles_lds<D, XS>(pl),
                           stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
