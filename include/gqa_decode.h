@@ -95,8 +95,13 @@ typedef enum gqa_status {
  * partition_size > 0 (a multiple of 32, at most 1 << 20) selects the
  * kernel-map page's fixed decomposition ("paged_attention_v1" up to
  * v1_max_ctx tokens, "paged_attention_v2" with partitions of partition_size
- * tokens above it), one workgroup per partition; gqa_policy_pages() gives the
- * policy page's AttentionConfig values (partition 512, threshold 8192).
+ * tokens above it); gqa_policy_pages() gives the policy page's
+ * AttentionConfig values (partition 512, threshold 8192).  Its work items are
+ * (partition, group of KV heads); a single-pass sequence stays one item,
+ * computed by one workgroup whose waves split its tiles and merge in LDS.  A
+ * contiguous cache launches one workgroup per item; a paged cache first lists
+ * its items in the workspace, largest first, and then launches no more
+ * workgroups than there can be items, taking them in that order.
  *
  * v1_max_ctx >= 0.  phases selects which kernels a call launches: 0 or 3 =
  * both, 1 = partition kernel only, 2 = merge kernel only (the merge then reads
@@ -142,12 +147,19 @@ void gqa_policy_default(gqa_policy_t* p);
 void gqa_policy_pages(gqa_policy_t* p);
 
 /*
- * Bytes of workspace gqa_decode / gqa_decode_contiguous need for these sizes
- * (max_ctx = max_blocks_per_seq * block_size, or s_kv).  0 when no sequence
- * can be split.  The workspace holds fp32 partial triples (m, l, O) and, for
- * the balanced decomposition, one 16-byte record per (sequence, head group)
- * (plus one counter per (sequence, head group) with GQA_POLICY_FUSED_MERGE);
- * its contents need no initialisation, except under GQA_POLICY_FUSED_MERGE
+ * Bytes of workspace gqa_decode / gqa_decode_xsplit / gqa_decode_contiguous
+ * need for these sizes (max_ctx = max_blocks_per_seq * block_size, or s_kv);
+ * the size covers both cache layouts.  The workspace holds the fp32 partial
+ * triples (m, l, O) of split sequences (kernel-map page, "paged_attention_v2":
+ * fp32 max_logits, exp_sum and partial outputs) and:
+ *   balanced decomposition: one 16-byte record per (sequence, head group),
+ *     plus one counter per (sequence, head group) with GQA_POLICY_FUSED_MERGE;
+ *     0 bytes in all when no sequence can be split;
+ *   fixed decomposition: for a paged cache, a 256-byte header and a work
+ *     list of up to one 8-byte item per (sequence, KV head, partition), even
+ *     when no sequence can be split (a contiguous cache needs no list).
+ * h_kv is needed because records and items are counted per KV head group.
+ * Its contents need no initialisation, except under GQA_POLICY_FUSED_MERGE
  * (see gqa_policy_t).  policy NULL means gqa_policy_default().
  * Returns 0 for invalid arguments.
  */
@@ -226,8 +238,13 @@ gqa_status_t gqa_decode_noalloc(const void* q, const void* k_cache, const void* 
 
 /*
  * Contiguous decode: every sequence holds s_kv tokens (s_kv >= 0) in a
- * [num_seqs, s_kv, h_kv, d_head] cache; with s_kv == 0 the output is zero and
- * k, v may be NULL.  Same rules as gqa_decode otherwise.
+ * [num_seqs, s_kv, h_kv, d_head] cache, one (S_kv, h_kv * d_head) row-major
+ * slab per sequence as in the decode-long page's tensor-layout docstring
+ * ("GQA fused-attention decode kernel -- long context"); q and out are
+ * [num_seqs, h_q, d_head] (kernel-map page, "paged_attention_v1" query
+ * layout).  With s_kv == 0 the output is zero and k, v may be NULL.  Same
+ * rules as gqa_decode otherwise; the workspace may be NULL when
+ * gqa_decode_ex_workspace_size() for this layout is 0.
  */
 gqa_status_t gqa_decode_contiguous(const void* q, const void* k, const void* v, void* out,
                                    int num_seqs, int s_kv, int h_q, int h_kv, int d_head,
