@@ -253,10 +253,12 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     return res
 
 
-def _cpu_worker(name: str, w: int, n: int, budget_s: float, barrier, results):
-    """One oracle worker: rebuilds the seeded workload, waits for the others,
-    then walks its share of the (sequence, KV head) slices (every n-th of a
-    seeded order, repeated) for budget_s of wall time with one BLAS thread."""
+def _cpu_worker(name: str, w: int, n: int, budget_s: float) -> int:
+    """One oracle worker process (bench.py --cpu-worker NAME W N BUDGET): builds
+    the seeded workload, prints "ready" and waits for a line on stdin, then
+    walks its share of the (sequence, KV head) slices (every n-th of a seeded
+    order, repeated) for budget_s of wall time with one BLAS thread, and prints
+    its counts as one JSON line."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import reference as R
@@ -268,7 +270,8 @@ def _cpu_worker(name: str, w: int, n: int, budget_s: float, barrier, results):
     mine = [pairs[i] for i in order[w::n]] or [pairs[order[w % len(pairs)]]]
     done_bytes, done_pairs = 0, 0
     with threadpool_limits(limits=1):
-        barrier.wait()
+        print("ready", flush=True)
+        sys.stdin.readline()                      # the start signal, sent to all workers at once
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
             s, j = mine[done_pairs % len(mine)]
@@ -276,12 +279,8 @@ def _cpu_worker(name: str, w: int, n: int, budget_s: float, barrier, results):
             done_bytes += int(case.ctx_lens[s]) * case.d * 2 * 2
             done_pairs += 1
         elapsed = time.perf_counter() - t0
-    results.put((done_bytes, done_pairs, elapsed))
-
-
-def _gpu_initialised() -> bool:
-    torch = sys.modules.get("torch")
-    return bool(torch is not None and torch.cuda.is_initialized())
+    print(json.dumps({"bytes": done_bytes, "pairs": done_pairs, "seconds": elapsed}), flush=True)
+    return 0
 
 
 def cpu_baseline(name: str, budget_s: float = 10.0):
@@ -289,37 +288,40 @@ def cpu_baseline(name: str, budget_s: float = 10.0):
     worker processes (one per available core, at most CPU_WORKERS_MAX), each
     with one BLAS thread, over whole (sequence, KV head) slices for about
     budget_s of wall time.  Rate = all workers' K/V bytes / the longest
-    worker's time.  The workers are forked before this process uses the GPU
-    (spawned if it already has), and every one of them is joined, or
-    terminated, before this returns: no child process outlives the call."""
-    import multiprocessing as mp
+    worker's time.  The workers are fresh Python processes (this script with
+    --cpu-worker), started together once every one has built its inputs; each
+    is waited for, or killed, before this returns, so no child process
+    outlives the call."""
+    import subprocess
 
     available = len(os.sched_getaffinity(0))
     n = max(1, min(CPU_WORKERS_MAX, available))
-    ctx = mp.get_context("spawn" if _gpu_initialised() else "fork")
-    barrier = ctx.Barrier(n)
-    results = ctx.SimpleQueue()               # no feeder thread to outlive the call
-    procs = [ctx.Process(target=_cpu_worker, args=(name, w, n, budget_s, barrier, results))
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker", name,
+                               str(w), str(n), repr(budget_s)],
+                              stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True, env=env)
              for w in range(n)]
+    got = []
     try:
         for p in procs:
-            p.start()
-        got = [results.get() for _ in procs]
+            if p.stdout.readline().strip() != "ready":
+                raise RuntimeError("an oracle worker failed to start")
+        for p in procs:                           # start them together
+            p.stdin.write("go\n")
+            p.stdin.flush()
+        for p in procs:
+            out, _ = p.communicate(timeout=budget_s + 600)
+            got.append(json.loads(out.strip().splitlines()[-1]))
+            if p.returncode != 0:
+                raise RuntimeError(f"an oracle worker exited with {p.returncode}")
     finally:
         for p in procs:
-            if p.pid is not None:
-                p.join(timeout=30)
-        for p in procs:
-            if p.is_alive():
-                p.terminate()
-                p.join(timeout=10)
-        for p in procs:
-            if p.pid is not None:
-                p.close()
-        results.close()
-    done_bytes = sum(g[0] for g in got)
-    done_pairs = sum(g[1] for g in got)
-    t_used = max(g[2] for g in got)
+            if p.poll() is None:
+                p.kill()
+            p.wait()
+    done_bytes = sum(g["bytes"] for g in got)
+    done_pairs = sum(g["pairs"] for g in got)
+    t_used = max(g["seconds"] for g in got)
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
             "host_cores": os.cpu_count(), "available_cores": available,
             "sample": (f"{done_pairs} (sequence, KV head) slices of {name} over {n} worker "
@@ -541,10 +543,15 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run one torch copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--cpu-worker", nargs=4, metavar=("WORKLOAD", "W", "N", "BUDGET"),
+                    help=argparse.SUPPRESS)
     ap.add_argument("--record-traffic", metavar="WORKLOAD/POLICY",
                     help="with --summarize-rocprof: store the traffic record in profiles/traffic.json")
     args = ap.parse_args()
 
+    if args.cpu_worker:
+        wl, w, n, budget = args.cpu_worker
+        return _cpu_worker(wl, int(w), int(n), float(budget))
     if args.summarize_rocprof:
         text, rec = summarize_rocprof(args.summarize_rocprof)
         print(text)
