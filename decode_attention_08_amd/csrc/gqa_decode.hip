@@ -13,8 +13,10 @@
 //                      stores the normalised output (the segment is the whole
 //                      sequence; kernel-map page, "paged_attention_v1") or
 //                      the fp32 partial (kernel-map page, "paged_attention_v2").
-//                      Two schedulers feed them: fixed partitions (one
-//                      workgroup each) and a balanced persistent grid.
+//                      Two schedulers feed them: a balanced persistent grid
+//                      and the pages' fixed partitions (one workgroup per
+//                      item; on a paged cache a planner kernel first lists
+//                      the items largest first).
 //   merge kernels      1 to 64 slots of 16 lanes per (sequence, query head)
 //                      of a split sequence: the n-ary form of
 //                      "_merge_running" over the partials, then the
@@ -30,13 +32,13 @@
 // head never leaves its lane group; only the tile max is exchanged between
 // the four 16-lane groups.  K feeds the A operand straight from HBM with
 // 16-byte loads (8 consecutive d of one token per lane).  V needs tokens
-// along the operand's K side, so with the row layouts each wave stages its V
-// tile in LDS with coalesced 16-byte stores and reads it back transposed (the
-// x-split layout stores V transposed already).  Up to d = 128 every wave
-// keeps the next tile's K and V loads in flight while it computes the current
-// one, and issues them only once the current tile has landed (one tile of
-// loads outstanding per wave).  K and V are read once, with non-temporal
-// loads.
+// along the operand's K side, so with the row layouts each wave's V tile goes
+// from HBM straight into LDS (global_load_lds) and is read back transposed
+// (ds_read_b64_tr_b16); the x-split layout stores V transposed already.  Every
+// wave keeps the next tile's K and V loads in flight while it computes the
+// current one, and issues them only once the current tile has landed (one
+// tile of loads outstanding per wave; the x-split layout at d = 256 keeps one
+// tile and no prefetch).  K and V are read once, with non-temporal loads.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
