@@ -240,10 +240,11 @@ struct Geo {
 constexpr bool kVdma = true;
 
 // LDS of one wave of the matrix-core segment code, in uint16: its V tiles
-// (row layouts), or one tile for the sub-wave state exchange (x-split).
-template <int D, bool XS>
+// (row layouts), each followed by its K tile when K also goes through LDS
+// (KD), or one tile for the sub-wave state exchange (x-split).
+template <int D, bool XS, bool KD = false>
 __host__ __device__ constexpr int wave_lds_elems() {
-  return (!XS && kVdma ? 2 : 1) * Geo<D>::V_TILE;
+  return (!XS && kVdma ? 2 : 1) * (KD ? 2 : 1) * Geo<D>::V_TILE;
 }
 
 // ------------------------------------------------- one wave, one segment --
@@ -266,13 +267,20 @@ __host__ __device__ constexpr int wave_lds_elems() {
 // P.V product needs, so V goes from HBM to the matrix core without the LDS
 // tile.
 
-template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
+// KD (row layouts, d <= 128) sends K through LDS as well: each instruction
+// then reads 4 whole 256-byte head slices of token rows (the V pattern)
+// instead of 64 bytes of 16 rows, and the matrix-core operand is read back
+// with 16-byte LDS reads.  It pays where a workgroup reads one KV head, 256 B
+// of each token row (the paged fixed decomposition's single-pass items), and
+// costs a little where four waves already read 1 KB runs of each row.
+template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT, bool KD = false>
 __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, uint16_t* vt,
                                              float2* mlx, int s, int j, int t0, int t1,
                                              bool complete, float2* pml,
                                              int64_t ml_stride, float* po, int64_t o_stride) {
   using Gm = Geo<D>;
   constexpr int KK = Gm::KK, NB = Gm::NB, CH = Gm::CH, RPI = Gm::RPI, NIT = Gm::NIT;
+  static_assert(!KD || (!XS && kVdma && D <= 128), "K through LDS: row layouts, d <= 128");
   // uniform over the wave; say so, so that addressing and branches stay scalar
   s = __builtin_amdgcn_readfirstlane(s);
   j = __builtin_amdgcn_readfirstlane(j);
@@ -324,7 +332,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   const int bs_mask = (1 << a.bs_shift) - 1;
 
   struct TileRows {
-    uint4_t k[2][KK];
+    uint4_t k[KD ? 1 : 2][KD ? 1 : KK];          // (KD: K goes to LDS, not registers)
     uint4_t v[kVdma ? 1 : NIT];                  // (kVdma: V goes to LDS, not registers)
   };
   struct TileX {
@@ -408,12 +416,29 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
           T.v[it] = load_stream<uint4_t, NT>(vb[hb] + off);
         }
       }
+      if constexpr (KD) {
+        // the K tile after the V tile: lane l fills position l % CH of row r
+        // with chunk (l % CH) ^ (r % CH), so that the 16 rows an operand read
+        // touches at one chunk fall in distinct LDS banks
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
+        for (int it = 0; it < NIT; ++it) {
+          const int r = it * RPI + lane / CH;
+          const int hb = r >> 4;
+          const int c = (lane % CH) ^ (r & (CH - 1));
+          const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + c * 8;
+          __builtin_amdgcn_global_load_lds(
+              reinterpret_cast<const void*>(kb[hb] + off),
+              (__attribute__((address_space(3))) void*)(vbuf + Gm::V_TILE + it * 64 * 8), 16, 0,
+              NT ? kAuxNontemporal : 0);
+        }
+      } else {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          T.k[hb][kk] = load_stream<uint4_t, NT>(kb[hb] + roff + 8 * (kk * 4 + grp));
+        for (int hb = 0; hb < 2; ++hb) {
+          const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            T.k[hb][kk] = load_stream<uint4_t, NT>(kb[hb] + roff + 8 * (kk * 4 + grp));
+        }
       }
     }
   };
@@ -435,7 +460,17 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
     for (int hb = 0; hb < 2; ++hb) {
       sc[hb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc[hb] = DT::mfma(T.k[hb][kk], qop[kk], sc[hb]);
+      for (int kk = 0; kk < KK; ++kk) {
+        uint4_t kop;
+        if constexpr (KD) {
+          const int row = 16 * hb + col;
+          const int pos = (kk * 4 + grp) ^ (row & (CH - 1));
+          kop = *reinterpret_cast<const uint4_t*>(vbuf + Gm::V_TILE + row * D + pos * 8);
+        } else {
+          kop = T.k[hb][kk];
+        }
+        sc[hb] = DT::mfma(kop, qop[kk], sc[hb]);
+      }
     }
     // online softmax (base 2); the lane holds tokens slot_token(grp, e) of head col
     float x[8];
@@ -543,9 +578,10 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   //      so a wave never has more than one tile of loads outstanding.
   int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   // V buffers: with kVdma (row layouts) tile A stages into vt and tile B into
-  // the wave's second tile; otherwise both stage through registers into vt
+  // the wave's second tile (with KD each V tile is followed by its K tile);
+  // otherwise both stage through registers into vt
   uint16_t* const vbA = vt;
-  uint16_t* const vbB = (!XS && kVdma) ? vt + Geo<D>::V_TILE : vt;
+  uint16_t* const vbB = (!XS && kVdma) ? vt + (KD ? 2 : 1) * Geo<D>::V_TILE : vt;
   if constexpr (D > 128 && !(kVdma && !XS)) {
     // d = 256 with V in registers: one register tile (32 KB of K/V per wave).
     // A wave waits for each tile; the other waves of the CU keep 3 x 32 KB in
@@ -608,7 +644,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
         const float a1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         const float a2 = o2.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o2.x - m_new);
         const float4_t* other =
-            reinterpret_cast<const float4_t*>(smem + w2 * wave_lds_elems<D, XS>());
+            reinterpret_cast<const float4_t*>(smem + w2 * wave_lds_elems<D, XS, KD>());
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = acc[nb] * a1 + other[nb * 64 + lane] * a2;
         l_run = l_run * a1 + o2.y * a2;
@@ -1058,7 +1094,7 @@ __global__ __launch_bounds__(kPlanThreads) void fixed_plan_kernel(Params a) {
 }
 
 // One item: partition p of sequence s for KV head j (this wave's head).
-template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT>
+template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT, bool KD = false>
 __device__ __forceinline__ void fixed_item(const Params& b, uint16_t* smem, float2* mlx, int w,
                                            int s, int j, int p) {
   const int L = seq_len<PAGED>(b, s);
@@ -1066,8 +1102,8 @@ __device__ __forceinline__ void fixed_item(const Params& b, uint16_t* smem, floa
   const int t0 = split ? p * b.part_size : 0;
   const int t1 = split ? min(t0 + b.part_size, L) : L;
   const int64_t row0 = ((int64_t)s * b.h_kv + j) * b.ncol;   // partial rows per (s, j, column)
-  wave_segment<DT, D, PAGED, XS, NT, SPLIT>(
-      b, smem, smem + ((XS && !SPLIT) ? 0 : w * wave_lds_elems<D, XS>()), mlx, s, j, t0, t1, !split,
+  wave_segment<DT, D, PAGED, XS, NT, SPLIT, KD>(
+      b, smem, smem + ((XS && !SPLIT) ? 0 : w * wave_lds_elems<D, XS, KD>()), mlx, s, j, t0, t1, !split,
       b.part_ml + row0 * b.max_parts + p, b.max_parts, b.part_o + (row0 * b.max_parts + p) * D,
       (int64_t)b.max_parts * D);
 }
@@ -1097,6 +1133,10 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
 // LDS.
 constexpr int kFixedPagedWaves = 4;
 constexpr size_t kFixedPagedLds = 96 * 1024;
+// K through LDS as well (wave_segment's KD): single-pass items read one KV head
+// of each token row.  Same box, pages' policy, us per step: paged_b64 197.3 ->
+// 177.6, mixed_b256 342.5 -> 320.4.
+__host__ __device__ constexpr bool fixed_paged_kd(int d, bool xs) { return !xs && d <= 128; }
 
 template <class DT, int D, bool XS>
 __global__ __launch_bounds__(kFixedPagedWaves * 64) void partition_fixed_paged_kernel(Params a) {
@@ -1112,7 +1152,8 @@ __global__ __launch_bounds__(kFixedPagedWaves * 64) void partition_fixed_paged_k
     Params b = a;
     b.hpw = 1 << (code & 3);                       // heads of this item
     b.wph = kFixedPagedWaves >> (code & 3);        // waves per head
-    fixed_item<DT, D, true, XS, true, true>(b, smem, mlx, w, s, j0 + w % b.hpw, code >> 2);
+    fixed_item<DT, D, true, XS, true, true, fixed_paged_kd(D, XS)>(b, smem, mlx, w, s,
+                                                                  j0 + w % b.hpw, code >> 2);
   }
 }
 
@@ -1900,8 +1941,10 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       const int grid = (int)std::min(bound, kFixedGridCap);
       if (hipLaunchKernel(reinterpret_cast<const void*>(&partition_fixed_paged_kernel<DT, D, XS>),
                           dim3(grid), dim3(64 * kFixedPagedWaves), args,
-                          std::max(kFixedPagedLds, (size_t)kFixedPagedWaves *
-                                                       wave_lds_elems<D, XS>() * sizeof(uint16_t)),
+                          std::max(kFixedPagedLds,
+                                   (size_t)kFixedPagedWaves *
+                                       wave_lds_elems<D, XS, fixed_paged_kd(D, XS)>() *
+                                       sizeof(uint16_t)),
                           stream) != hipSuccess)
         return GQA_ERR_LAUNCH;
     } else {
