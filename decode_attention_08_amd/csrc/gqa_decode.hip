@@ -1259,7 +1259,11 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   const int nw = blockDim.x >> 6;                // = hpw * wph
   // per-wave tiles: V staging (row layout) and the sub-wave state exchange;
   // the x-split layout with one wave per head needs neither
-  constexpr int tile_elems = VC > 0 ? dot2_wave_elems(VC) : (XS && !SPLIT) ? 0 : wave_lds_elems<D, XS>();
+  // SPLIT (one or two KV heads, one head's 256 B of each token row per wave):
+  // K goes through LDS as well (wave_segment's KD)
+  constexpr bool KDB = SPLIT && !XS && D <= 128;
+  constexpr int tile_elems =
+      VC > 0 ? dot2_wave_elems(VC) : (XS && !SPLIT) ? 0 : wave_lds_elems<D, XS, KDB>();
   uint16_t* const vt = smem + w * tile_elems;
   int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * tile_elems);
 
@@ -1343,8 +1347,8 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
       if constexpr (VC > 0)
         wave_segment_dot2<DT, PAGED, VC>(a, vt, s, j, t0, t1, complete, pml, 1, po, D);
       else
-        wave_segment<DT, D, PAGED, XS, true, SPLIT>(a, smem, vt, mlx, s, j, t0, t1, complete, pml,
-                                                    1, po, D);
+        wave_segment<DT, D, PAGED, XS, true, SPLIT, KDB>(a, smem, vt, mlx, s, j, t0, t1, complete,
+                                                         pml, 1, po, D);
       // (a contiguous cache's records are arithmetic: the merge recomputes them)
       if (PAGED && threadIdx.x == 0) {
         if (complete) {
@@ -1664,6 +1668,13 @@ int heads_per_group(int h_kv, int d) {
   return 1;
 }
 
+// Waves of a balanced workgroup whose one or two KV heads split their
+// segments.  Four waves, with K and V through LDS, beat eight waves with K in
+// registers (same box, us per step: tiny_contig 5.8 -> 5.2; 64 paged sequences
+// of 512-8192 tokens, 16/2 heads, 52.8-53.2 -> 50.7-51.4; 4 sequences of 32768
+// tokens, 16/1 heads, 20.7 -> 19.6-20.0).
+constexpr int kSplitWaves = 4;
+
 // How a call is decomposed once the sizes are known.
 struct Plan {
   bool balanced;
@@ -1742,12 +1753,13 @@ Plan make_plan(int num_seqs, int t_q, int h_q, int h_kv, int d, int max_ctx,
   // the balanced scheduler keeps its per-sequence prefix in LDS as int32
   pl.balanced = pol.partition_size == 0 && num_seqs <= kMaxSeqsBalanced &&
                 upper_tiles(num_seqs, pl.n_groups, max_ctx) < (int64_t)INT32_MAX / 2;
-  // Groups of one or two KV heads (small h_kv) get several waves per head,
-  // which split each segment's tiles: a lone wave per head walking a short
-  // sequence is latency-bound.  Larger groups have waves enough; on a batch of
-  // 256 sequences of ~3400 tokens with four KV heads the split cost 2%.
+  // Groups of one or two KV heads (small h_kv) get kSplitWaves / hpw waves per
+  // head, which split each segment's tiles: a lone wave per head walking a
+  // short sequence is latency-bound.  Larger groups have waves enough; on a
+  // batch of 256 sequences of ~3400 tokens with four KV heads the split cost
+  // 2%.
   if (pl.balanced && pl.hpw <= 2 && !(pol.flags & (GQA_POLICY_FUSED_MERGE | GQA_POLICY_VALU_DOT2)))
-    pl.wph = max_heads_per_group(d) / pl.hpw;
+    pl.wph = kSplitWaves / pl.hpw;
   if (pl.balanced && (pol.flags & GQA_POLICY_VALU_DOT2))
     pl.vc = (h_q / h_kv) * t_q <= 4 ? 4 : 8;
   pl.part_size = pol.partition_size > 0 ? pol.partition_size : kFallbackPartition;
@@ -1825,6 +1837,8 @@ int resident_grid(const void* kernel, int block, size_t dyn_lds_exact, int* cus_
 template <int D, bool XS>
 size_t tiles_lds(const Plan& pl) {
   if (pl.vc > 0) return (size_t)pl.hpw * dot2_wave_elems(pl.vc) * sizeof(uint16_t);
+  if (pl.balanced && pl.wph > 1 && !XS && D <= 128)   // split: K through LDS too
+    return (size_t)pl.hpw * pl.wph * wave_lds_elems<D, XS, true>() * sizeof(uint16_t);
   return (XS && pl.wph == 1) ? 0
                              : (size_t)pl.hpw * pl.wph * wave_lds_elems<D, XS>() * sizeof(uint16_t);
 }
