@@ -183,23 +183,28 @@ def _torch_stream(stream, device):
 
 def check_block_table(block_table: torch.Tensor, ctx_lens: torch.Tensor, num_blocks: int,
                       block_size: int) -> None:
-    """Checked mode for block ids, on a host copy, before anything is launched.
+    """Checked mode for the paging data, on a host copy, before anything is
+    launched.
 
-    Token t of sequence s lives in block block_table[s, t // block_size]
-    (kernel-map page, "paged_attention_v1", the block-table addressing of its
-    key_cache).  Every entry the kernels will read (sequence s, entry e with
-    e < ceil(L_s / block_size), L_s = ctx_lens[s] clamped to
-    [0, max_blocks_per_seq * block_size] as the kernels clamp it) must name a
-    block of the pool: 0 <= id < num_blocks.  Raises ValueError naming the
-    first offending (sequence, entry, id).  Entries past a sequence's length
-    are never read and are not checked."""
+    ctx_lens[s] must lie in [0, max_blocks_per_seq * block_size] (the kernels
+    would clamp it silently).  Token t of sequence s lives in block
+    block_table[s, t // block_size] (kernel-map page, "paged_attention_v1", the
+    block-table addressing of its key_cache), so every entry the kernels will
+    read (sequence s, entry e < ceil(L_s / block_size)) must name a block of the
+    pool: 0 <= id < num_blocks.  Raises ValueError naming the first offending
+    length or (sequence, entry, id).  Entries past a sequence's length are
+    never read and are not checked."""
     import numpy as np
     bt = block_table.detach().to("cpu").numpy()
     lens = ctx_lens.detach().to("cpu").numpy().astype(np.int64)
     _require(bt.ndim == 2 and lens.ndim == 1 and bt.shape[0] == lens.shape[0],
              "block_table must be [num_seqs, max_blocks] and ctx_lens [num_seqs]")
     max_blocks = bt.shape[1]
-    lens = lens.clip(0, max_blocks * block_size)
+    bad_len = (lens < 0) | (lens > max_blocks * block_size)
+    if bad_len.any():
+        s = int(np.argmax(bad_len))
+        raise ValueError(f"ctx_lens[{s}] = {int(lens[s])} is outside [0, {max_blocks * block_size}] "
+                         f"(max_blocks_per_seq {max_blocks} x block_size {block_size})")
     used = (lens + block_size - 1) // block_size
     live = np.arange(max_blocks)[None, :] < used[:, None]
     bad = live & ((bt < 0) | (bt >= num_blocks))

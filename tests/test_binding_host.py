@@ -30,14 +30,22 @@ def test_entries_past_the_length_are_not_checked():
     # sequence 0 reads ceil(17/16) = 2 blocks: the -1 and 99 after them are never read
     q, k, v, bt, ctx = _paged_inputs([[0, 1, 99], [2, -1, -1]], [17, 16])
     gq.check_block_table(bt, ctx, 6, 16)
-    # lengths are clamped to max_blocks * block_size as the kernels clamp them
-    _, _, _, bt2, ctx2 = _paged_inputs([[0, 1, 2]], [10 ** 6])
+    # a full table at the largest length is fine, one block short of the pool is not
+    _, _, _, bt2, ctx2 = _paged_inputs([[0, 1, 2]], [48])
     gq.check_block_table(bt2, ctx2, 3, 16)
     with pytest.raises(ValueError, match="outside the pool of 2"):
         gq.check_block_table(bt2, ctx2, 2, 16)
-    # negative lengths read nothing
-    gq.check_block_table(torch.tensor([[-5]], dtype=torch.int32),
-                         torch.tensor([-3], dtype=torch.int32), 1, 16)
+
+
+def test_lengths_outside_the_table_rejected():
+    """The kernels clamp ctx_lens to [0, max_blocks * block_size]; the checked
+    mode reports such lengths instead."""
+    _, _, _, bt, ctx = _paged_inputs([[0, 1, 2]], [49])
+    with pytest.raises(ValueError, match=r"ctx_lens\[0\] = 49 is outside \[0, 48\]"):
+        gq.check_block_table(bt, ctx, 3, 16)
+    with pytest.raises(ValueError, match=r"ctx_lens\[1\] = -3"):
+        gq.check_block_table(torch.tensor([[0], [1]], dtype=torch.int32),
+                             torch.tensor([5, -3], dtype=torch.int32), 2, 16)
 
 
 def test_valid_table_passes_the_check_then_needs_a_gpu():
