@@ -1021,8 +1021,9 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
 // equal and the host knows their number; one workgroup per item.
 //
 // Paged cache: the planner kernel (one workgroup) lists the items in the
-// workspace longest first, by a counting sort over their size (tokens times
-// heads), and the partition kernel takes item b, b + grid, ... in list order
+// workspace largest first, by a counting sort over their size (tokens times
+// heads; each thread writes the items of its sequences), and the partition
+// kernel takes item b, b + grid, ... in list order
 // (a grid of at most kFixedGridCap workgroups, no larger than the items can
 // be), so the hardware dispatcher starts the longest items first and hands
 // each CU the next item as it frees up.  Single-pass items take the host's
@@ -1140,7 +1141,7 @@ __host__ __device__ constexpr bool fixed_paged_kd(int d, bool xs) { return !xs &
 
 template <class DT, int D, bool XS>
 __global__ __launch_bounds__(kFixedPagedWaves * 64) void partition_fixed_paged_kernel(Params a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V tiles per wave
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // V and K tiles per wave
   __shared__ float2 mlx[kFixedPagedWaves * 16];                      // sub-wave (m, l) exchange
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_items = a.fixed_hdr[0];
