@@ -4,9 +4,10 @@ the float64 oracle on every output row (tolerance of tests/parity.py).
 Each case draws: the cache layout (contiguous, paged rows, paged x-split), the
 dtype, d_head, KV heads and group size with G * T_q <= 16, T_q, the block
 size, 1-9 sequence lengths (zero, one token, block and tile edges, and lengths
-past the pages' single-pass threshold), spare NaN blocks, a scale, and a
-policy (balanced with a random single-pass bound, or fixed partitions of a
-random multiple of 32).  The draws are printed before each case runs."""
+past the pages' single-pass threshold), spare NaN blocks, a scale (kept
+moderate for bf16 at d >= 128, see _draw), and a policy (balanced with a
+random single-pass bound, or fixed partitions of a random multiple of 32).
+The draws are printed before each case runs."""
 import numpy as np
 import pytest
 import torch
@@ -41,6 +42,11 @@ def _draw(i):
     lens = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(0, 6000))
             for _ in range(n)]
     scale = float(rng.choice([1.0 / np.sqrt(d), 0.02, 0.3]))
+    if dtype == W.BF16 and scale == 0.3 and d >= 128:
+        # logits of spread 0.3 sqrt(d) make the softmax nearly one-hot, and an
+        # output that is then a single V value in [4, 8) moves by up to 1.6e-2
+        # when it is rounded to bf16, beyond the 1e-2 bound for any kernel
+        scale = 1.0 / np.sqrt(d)
     if rng.random() < 0.5:
         pol = ("balanced", 0, int(rng.choice([0, 64, 256, 1000, 1 << 30])))
     else:
