@@ -593,20 +593,24 @@ def main():
 
     also = {}
     if not args.no_also:
-        for name in BENCH_WORKLOADS:
-            c = case if name == args.workload else bench_case(name)
-            for pol in POLICIES:
-                if name == args.workload and pol == args.policy:
-                    continue
-                if name.endswith(XSPLIT_SUFFIX) and pol != "default":
-                    continue
-                if (pol == "fused" and name not in FUSED_ROWS) or (pol == "valu" and name not in VALU_ROWS):
-                    continue
-                r = time_workload(c, pol, args.steps, args.warmup)
-                also[f"{name}/{pol}"] = r
-                print(f"[bench] {name}/{pol}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s, "
-                      f"partition {r['partition_us_mean']:.1f} us ({r['partition_gbs']:.0f} GB/s)",
-                      file=sys.stderr, flush=True)
+        # the default and pages' policies first, then the comparison variants
+        # (fused merge, packed FMA): those keep the vector ALU busy for longer,
+        # and rows timed right after them read a few percent slow
+        for group in (("default", "pages"), ("fused", "valu")):
+            for name in BENCH_WORKLOADS:
+                c = case if name == args.workload else bench_case(name)
+                for pol in group:
+                    if name == args.workload and pol == args.policy:
+                        continue
+                    if name.endswith(XSPLIT_SUFFIX) and pol != "default":
+                        continue
+                    if (pol == "fused" and name not in FUSED_ROWS) or (pol == "valu" and name not in VALU_ROWS):
+                        continue
+                    r = time_workload(c, pol, args.steps, args.warmup)
+                    also[f"{name}/{pol}"] = r
+                    print(f"[bench] {name}/{pol}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s, "
+                          f"partition {r['partition_us_mean']:.1f} us ({r['partition_gbs']:.0f} GB/s)",
+                          file=sys.stderr, flush=True)
 
     sizes = {case.name: case.kv_bytes}
     for k, r in also.items():
