@@ -211,6 +211,39 @@ __device__ __forceinline__ void wave_lds_fence() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Device-coherent vector memory access: cache policy sc1, the bits the
+// compiler gives a relaxed device-scope atomic load or store on this
+// architecture.  Such a store writes through its XCD's L2 and such a load does
+// not take a line that another XCD may have changed from its own L2, so data
+// passed between workgroups this way needs no device-scope release or acquire
+// fence (which write back or invalidate the whole L2 of the XCD), only the
+// completion of the stores before the atomic that publishes them.  Raw buffer
+// operations carry the 16-byte width the atomic forms lack; the resource spans
+// 2 GB from a wave-uniform base.
+constexpr int kAuxDeviceCoherent = 16;
+constexpr int kBufferWord3 = 0x00020000;        // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferWord3);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                               float4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_t, v), r, byte_off, 0,
+                                         kAuxDeviceCoherent);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                               float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_t, v), r, byte_off, 0,
+                                        kAuxDeviceCoherent);
+}
+__device__ __forceinline__ float4_t load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0,
+                                                                            kAuxDeviceCoherent));
+}
+__device__ __forceinline__ float2 load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0,
+                                                                         kAuxDeviceCoherent));
+}
+
 // Token held in k-slot e (0..7) of lane group grp: two 16-token halves, four
 // consecutive tokens each.  The same slot order feeds P^T and V^T.
 __device__ __forceinline__ int slot_token(int grp, int e) {
@@ -273,7 +306,11 @@ __host__ __device__ constexpr int wave_lds_elems() {
 // with 16-byte LDS reads.  It pays where a workgroup reads one KV head, 256 B
 // of each token row (the paged fixed decomposition's single-pass items), and
 // costs a little where four waves already read 1 KB runs of each row.
-template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT, bool KD = false>
+//
+// WT writes a partial with device-coherent stores (store_coherent) relative to
+// a.part_ml / a.part_o, for a merge by another workgroup of the same launch.
+template <class DT, int D, bool PAGED, bool XS, bool NT, bool SPLIT, bool KD = false,
+          bool WT = false>
 __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, uint16_t* vt,
                                              float2* mlx, int s, int j, int t0, int t1,
                                              bool complete, float2* pml,
@@ -669,6 +706,15 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
       }
       *reinterpret_cast<uint2*>(dst + 16 * nb) = make_uint2(w01, w23);
     }
+  } else if constexpr (WT) {
+    const uint32_t o0 = (uint32_t)((po - a.part_o) + (int64_t)col * o_stride + 4 * grp) * 4;
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) store_coherent(ro, o0 + 64 * nb, acc[nb]);
+    if (grp == 0)
+      store_coherent(coherent_rsrc(a.part_ml),
+                     (uint32_t)((pml - a.part_ml) + (int64_t)col * ml_stride) * 8,
+                     make_float2(m_run, l_run));
   } else {
     float* dst = po + (int64_t)col * o_stride + 4 * grp;
 #pragma unroll
@@ -1165,13 +1211,16 @@ __global__ __launch_bounds__(kFixedPagedWaves * 64) void partition_fixed_paged_k
 // over the range's n segments, in segment order, then "Final normalise +
 // store".  One 16-lane slot per partial row (a query row of the head group);
 // lane r holds d elements [r*D/16, (r+1)*D/16).  Partial k of the range sits
-// in slot `first` (k = 0) or 2 (wg0 + k), as the balanced kernel wrote it.
+// in slot `first` (k = 0) or 2 (wg0 + k), as the balanced kernel wrote it with
+// device-coherent stores; it is read back with device-coherent loads, U
+// partials in flight per lane.
 
 template <class DT, int D>
 __device__ __forceinline__ void fused_range_merge(const Params& a, int s, int hg, int wg0, int n,
                                                   int first) {
   constexpr int E = D / 16;
-  constexpr int U = 8;
+  constexpr int U = D <= 128 ? 16 : 8;
+  const __amdgpu_buffer_rsrc_t rml = coherent_rsrc(a.part_ml), ro = coherent_rsrc(a.part_o);
   const int heads = a.hpw * a.ncol;               // partial rows per slot
   const int nslot = blockDim.x / 16;
   const int r = threadIdx.x % 16;
@@ -1187,11 +1236,10 @@ __device__ __forceinline__ void fused_range_merge(const Params& a, int s, int hg
       for (int u = 0; u < U; ++u) {
         if (k0 + u < n) {
           const int k = k0 + u;
-          const int64_t rw = (int64_t)(k == 0 ? first : 2 * (wg0 + k)) * heads + row;
-          t2[u] = a.part_ml[rw];
-          const float4_t* src = reinterpret_cast<const float4_t*>(a.part_o + rw * D + r * E);
+          const uint32_t rw = (uint32_t)((k == 0 ? first : 2 * (wg0 + k)) * heads + row);
+          t2[u] = load_coherent2(rml, rw * 8);
 #pragma unroll
-          for (int e4 = 0; e4 < E / 4; ++e4) v[u][e4] = src[e4];
+          for (int e4 = 0; e4 < E / 4; ++e4) v[u][e4] = load_coherent4(ro, (rw * D + r * E + 4 * e4) * 4);
         }
       }
 #pragma unroll
@@ -1348,8 +1396,8 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
       if constexpr (VC > 0)
         wave_segment_dot2<DT, PAGED, VC>(a, vt, s, j, t0, t1, complete, pml, 1, po, D);
       else
-        wave_segment<DT, D, PAGED, XS, true, SPLIT, KDB>(a, smem, vt, mlx, s, j, t0, t1, complete,
-                                                         pml, 1, po, D);
+        wave_segment<DT, D, PAGED, XS, true, SPLIT, KDB, FUSED>(a, smem, vt, mlx, s, j, t0, t1,
+                                                                complete, pml, 1, po, D);
       // (a contiguous cache's records are arithmetic: the merge recomputes them)
       if (PAGED && threadIdx.x == 0) {
         if (complete) {
@@ -1359,27 +1407,28 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
         }
       }
       if (FUSED && !complete) {
-        // Fused merge.  Release this workgroup's partials, count it in, and let
-        // the workgroup that completes the count merge the range; it resets
-        // the counter for the next call.  Nothing waits on other workgroups.
-        // The barrier orders every wave's partial stores before thread 0's
-        // device-scope release, and thread 0's acquire before every wave's
-        // reads; one fence per workgroup matters, since on this part a
-        // device-scope fence writes back (release) or invalidates (acquire)
-        // the whole L2 of the XCD.
+        // Fused merge.  Publish this workgroup's partials, count it in, and
+        // let the workgroup that completes the count merge the range; it
+        // resets the counter for the next call.  Nothing waits on other
+        // workgroups.  The partials were written with device-coherent stores
+        // and are read with device-coherent loads, so no device-scope fence is
+        // needed (on this part one writes back or invalidates the whole L2 of
+        // the XCD): each wave waits until its stores have completed, the
+        // barrier then orders them before thread 0's device-scope atomic, and
+        // the merging waves issue their loads only after that atomic returned.
         const int wg0 = (int)(rs / chunk);       // the range's first and last shares
         const int n = (int)((re - 1) / chunk) - wg0 + 1;
+        wait_tile_loads();                       // vmcnt(0): loads and stores
         __syncthreads();
-        if (threadIdx.x == 0) {
-          __threadfence();
-          last_of_range = atomicAdd(a.cnt + r, 1) == n - 1;
-          if (last_of_range) __threadfence();
-        }
+        if (threadIdx.x == 0)
+          last_of_range = __hip_atomic_fetch_add(a.cnt + r, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == n - 1;
         __syncthreads();
         if (last_of_range) {
           const int first = 2 * wg0 + (rs == (int64_t)wg0 * chunk ? 0 : 1);
           fused_range_merge<DT, D>(a, s, hg, wg0, n, first);
-          if (threadIdx.x == 0) a.cnt[r] = 0;
+          if (threadIdx.x == 0)
+            __hip_atomic_store(a.cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();                         // last_of_range read before it is rewritten
       }

@@ -116,8 +116,11 @@ typedef enum gqa_status {
  * GQA_POLICY_FUSED_MERGE: the workgroup that finishes a split range last
  * merges that range itself (it finds out through a per-range atomic counter in
  * the workspace; nothing waits on anything), and no merge kernel is launched.
- * It saves the merge launch, but a range's merge then runs on one CU, so it
- * pays only for batches of many short split ranges.  Contract: the workspace
+ * Partials pass between workgroups through device-coherent stores and loads,
+ * with no device-scope fence.  It saves the merge launch, but a range's merge
+ * then runs on one CU at the end of the launch, so it can pay only for batches
+ * of many short split ranges (on MI355X it ties with the merge kernel on paged
+ * batches and loses where ranges are long).  Contract: the workspace
  * must be zero-filled before its first call with this flag (for instance when
  * it is allocated); every call that runs to completion leaves the counters at
  * zero again, graph replays included.  phases 2 then does nothing.

@@ -105,3 +105,40 @@ def test_fused_graph_replay(gq):
             assert torch.equal(out, eager), f"replay {rep}"
     assert_close(eager.float().cpu().numpy().astype(np.float64), R.decode(case), W.BF16,
                  what="fused graph")
+
+
+@pytest.mark.parametrize("layout,dtype", [("contiguous", W.F16), ("paged", W.BF16)])
+def test_fused_alternating_inputs_one_workspace(gq, layout, dtype):
+    """Partials pass between workgroups, often on different XCDs, without a
+    device-scope fence.  Alternate two queries on one workspace and check every
+    call against its own oracle result: a merge that read a partial of the
+    previous call (a stale cache line) would miss the tolerance by far, since
+    the second query is the first one negated and doubled."""
+    import dataclasses
+    if layout == "contiguous":
+        base = W.contiguous_case("fz_alt_c", 2700, 3, 32, 8, 128, 6000, dtype)
+    else:
+        base = W.paged_case("fz_alt_p", 2701, [6000, 900, 3000, 7000, 40, 2500], h_q=32,
+                            h_kv=8, d=128, dtype=dtype)
+    q32 = {W.F16: lambda b: b.view(np.float16).astype(np.float32)}.get(dtype)
+    if q32 is None:
+        def q32(b):
+            return (b.astype(np.uint32) << 16).view(np.float32)
+    other = dataclasses.replace(base, q=W.f32_to_storage_bits(-2.0 * q32(base.q), dtype))
+    cases = [base, other]
+    refs = [R.decode(c) for c in cases]
+    qs = [case_to_device(c, DEV)["q"] for c in cases]
+    dev = case_to_device(base, DEV)
+    kw = ({} if layout == "contiguous" else
+          dict(block_table=dev["block_table"], ctx_lens=dev["ctx_lens"]))
+    call = gq.prepare(dev["q"], dev["k"], dev["v"], scale=base.scale,
+                      policy=_fused(gq, v1_max_ctx=0), **kw)
+    out = call.out
+    for rep in range(6):
+        i = rep % 2
+        print(f"fused alternating {layout} rep={rep}", flush=True)
+        dev["q"].copy_(qs[i])
+        call()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert_close(got, refs[i], dtype, what=f"fused alternating {layout} rep {rep}")
