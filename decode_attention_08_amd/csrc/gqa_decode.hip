@@ -378,12 +378,13 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   };
   using Tile = std::conditional_t<XS, TileX, TileRows>;
 
-  // Issue every global load of the tile starting at token tb (tb < t1).  Each
+  // Issue the global loads of the tile starting at token tb (tb < t1): all of
+  // them (part 0), K only (part 1) or V only (part 2).  Each
   // 16-token half has a wave-uniform base pointer; lanes add small 32-bit
   // offsets.  Rows past t1 are clamped to the last live token of the segment,
   // so every load is in bounds and unconditional; those rows are masked
   // afterwards (score -inf, hence a zero weight on a finite V row).
-  auto load = [&](Tile& T, int tb, uint16_t* vbuf) {
+  auto load = [&](Tile& T, int tb, uint16_t* vbuf, int part = 0) {
     const uint16_t* kb[2];
     const uint16_t* vb[2];
     int last[2];                                  // last live row of each half
@@ -437,6 +438,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
       }
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
+        if (part == 1) break;
         const int r = it * RPI + lane / CH;
         const int hb = r >> 4;                      // uniform per instruction
         if constexpr (kVdma) {
@@ -468,7 +470,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
               (__attribute__((address_space(3))) void*)(vbuf + Gm::V_TILE + it * 64 * 8), 16, 0,
               NT ? kAuxNontemporal : 0);
         }
-      } else {
+      } else if (part != 2) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const uint32_t roff = (uint32_t)min(col, last[hb]) * tok_stride;
@@ -612,7 +614,8 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   //      are peeled, so every wait count the compiler derives is static; the
   //      scheduling barriers keep each prefetch ahead of the compute it
   //      overlaps.  The current tile has landed before the next one is issued,
-  //      so a wave never has more than one tile of loads outstanding.
+  //      so a wave never has more than one tile of loads outstanding (at
+  //      d = 256 with the row layouts, one tile plus the K half of the next).
   int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
   // V buffers: with kVdma (row layouts) tile A stages into vt and tile B into
   // the wave's second tile (with KD each V tile is followed by its K tile);
@@ -627,6 +630,38 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
     for (int tb = t0; n > 0; --n, tb += kTile) {
       load(A, tb, vbA);
       compute(A, tb, vbA);
+    }
+  } else if (D > 128 && !XS && kVdma && n > 0) {
+    // d = 256: K one tile further ahead than V, in three register tiles (V
+    // keeps its two LDS tiles, all the LDS four such waves can have).  Before
+    // tile t is computed, V(t+1) and K(t+2) are issued, and the wait for tile t
+    // lets K(t+1), issued after V(t), stay in flight.  Same box, us per
+    // partition launch on 2 sequences of 32768 tokens, 32/8 heads: 83.4 ->
+    // 81.9; at d = 128 the same order was 1-3% slower.
+    constexpr int NK = 2 * KK;                    // K load instructions per tile
+    Tile T0, T1, T2;
+    auto body = [&](Tile& Tc, Tile& Tn2, uint16_t* vc, uint16_t* vn, int t) {
+      const int tb = t0 + t * kTile;
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < n)
+        __builtin_amdgcn_s_waitcnt((NK & 15) | ((NK >> 4) << 14) | 0x0F70);   // vmcnt(NK)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);                                    // vmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < n) load(Tn2, tb + kTile, vn, 2);          // V(t+1)
+      if (t + 2 < n) load(Tn2, tb + 2 * kTile, vn, 1);      // K(t+2)
+      __builtin_amdgcn_sched_barrier(0);
+      compute(Tc, tb, vc);
+    };
+    load(T0, t0, vbA);
+    if (n > 1) load(T1, t0 + kTile, vbB, 1);
+    for (int t = 0; t < n; t += 6) {              // K tile t % 3, V tile t % 2
+      body(T0, T2, vbA, vbB, t);
+      if (t + 1 < n) body(T1, T0, vbB, vbA, t + 1);
+      if (t + 2 < n) body(T2, T1, vbA, vbB, t + 2);
+      if (t + 3 < n) body(T0, T2, vbB, vbA, t + 3);
+      if (t + 4 < n) body(T1, T0, vbA, vbB, t + 4);
+      if (t + 5 < n) body(T2, T1, vbB, vbA, t + 5);
     }
   } else if (n > 0) {
     Tile A, B;
