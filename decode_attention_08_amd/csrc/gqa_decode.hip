@@ -270,14 +270,13 @@ struct Geo {
 // 16 l), double-buffered so that the next tile's V lands while the current
 // one is read; the matrix-core operand V^T is then read back with the
 // transposing LDS read ds_read_b64_tr_b16.  No V passes through registers.
-constexpr bool kVdma = true;
 
 // LDS of one wave of the matrix-core segment code, in uint16: its V tiles
 // (row layouts), each followed by its K tile when K also goes through LDS
 // (KD), or one tile for the sub-wave state exchange (x-split).
 template <int D, bool XS, bool KD = false>
 __host__ __device__ constexpr int wave_lds_elems() {
-  return (!XS && kVdma ? 2 : 1) * (KD ? 2 : 1) * Geo<D>::V_TILE;
+  return (XS ? 1 : 2) * (KD ? 2 : 1) * Geo<D>::V_TILE;
 }
 
 // ------------------------------------------------- one wave, one segment --
@@ -317,7 +316,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
                                              int64_t ml_stride, float* po, int64_t o_stride) {
   using Gm = Geo<D>;
   constexpr int KK = Gm::KK, NB = Gm::NB, CH = Gm::CH, RPI = Gm::RPI, NIT = Gm::NIT;
-  static_assert(!KD || (!XS && kVdma && D <= 128), "K through LDS: row layouts, d <= 128");
+  static_assert(!KD || (!XS && D <= 128), "K through LDS: row layouts, d <= 128");
   // uniform over the wave; say so, so that addressing and branches stay scalar
   s = __builtin_amdgcn_readfirstlane(s);
   j = __builtin_amdgcn_readfirstlane(j);
@@ -368,9 +367,8 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   const uint32_t tok_stride = (uint32_t)a.h_kv * D;   // elements between consecutive tokens
   const int bs_mask = (1 << a.bs_shift) - 1;
 
-  struct TileRows {
-    uint4_t k[KD ? 1 : 2][KD ? 1 : KK];          // (KD: K goes to LDS, not registers)
-    uint4_t v[kVdma ? 1 : NIT];                  // (kVdma: V goes to LDS, not registers)
+  struct TileRows {                               // (V goes to LDS, not registers)
+    uint4_t k[KD ? 1 : 2][KD ? 1 : KK];          // (KD: K goes to LDS as well)
   };
   struct TileX {
     uint4_t k[2][KK];
@@ -441,19 +439,14 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
         if (part == 1) break;
         const int r = it * RPI + lane / CH;
         const int hb = r >> 4;                      // uniform per instruction
-        if constexpr (kVdma) {
-          // lane l fills LDS position l % CH of row r, which holds chunk
-          // (l % CH) ^ swizzle(r) of the row (the staged layout below)
-          const int c = (lane % CH) ^ v_swizzle(r);
-          const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + c * 8;
-          __builtin_amdgcn_global_load_lds(
-              reinterpret_cast<const void*>(vb[hb] + off),
-              (__attribute__((address_space(3))) void*)(vbuf + it * 64 * 8), 16, 0,
-              NT ? kAuxNontemporal : 0);
-        } else {
-          const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + (lane % CH) * 8;
-          T.v[it] = load_stream<uint4_t, NT>(vb[hb] + off);
-        }
+        // lane l fills LDS position l % CH of row r, which holds chunk
+        // (l % CH) ^ swizzle(r) of the row (the staged layout below)
+        const int c = (lane % CH) ^ v_swizzle(r);
+        const uint32_t off = (uint32_t)min(r & 15, last[hb]) * tok_stride + c * 8;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(vb[hb] + off),
+            (__attribute__((address_space(3))) void*)(vbuf + it * 64 * 8), 16, 0,
+            NT ? kAuxNontemporal : 0);
       }
       if constexpr (KD) {
         // the K tile after the V tile: lane l fills position l % CH of row r
@@ -484,15 +477,6 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
 
   // fold the tile starting at token tb into (m_run, l_run, acc)
   auto compute = [&](const Tile& T, int tb, const uint16_t* vbuf) {
-    if constexpr (!XS && !kVdma) {
-      // stage V: row r, chunk c at position c ^ swizzle(r)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int r = it * RPI + lane / CH;
-        const int pos = (lane % CH) ^ v_swizzle(r);
-        *reinterpret_cast<uint4_t*>(vt + r * D + pos * 8) = T.v[kVdma ? 0 : it];
-      }
-    }
     // scores S^T = K . Q^T
     float4_t sc[2];
 #pragma unroll
@@ -571,35 +555,21 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
       wave_lds_fence();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        uint4_t vop;
-        if constexpr (kVdma) {
-          // ds_read_b64_tr_b16: within each 16-lane group, lane i receives
-          // element i % 4 of the 8-byte loads of lanes 4 e + i / 4 (e = 0..3).
-          // Lane (col, grp) loads row slot_token(grp, col / 4) (then the same
-          // token + 16) at d = 16 nb + 4 (col % 4), so it receives
-          // V[slot_token(grp, e)][16 nb + col]: its V^T operand row.
-          const int d0 = 16 * nb + 4 * (col & 3);
-          const int r0 = slot_token(grp, col >> 2), r1 = r0 + 16;
-          typedef short short4_t __attribute__((ext_vector_type(4)));
-          typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
-              const_cast<uint16_t*>(vbuf) + r0 * D + (((d0 >> 3) ^ v_swizzle(r0)) << 3) + (d0 & 7)));
-          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
-              const_cast<uint16_t*>(vbuf) + r1 * D + (((d0 >> 3) ^ v_swizzle(r1)) << 3) + (d0 & 7)));
-          const uint2_t l2 = __builtin_bit_cast(uint2_t, lo), h2 = __builtin_bit_cast(uint2_t, hi);
-          vop = uint4_t{l2.x, l2.y, h2.x, h2.y};
-        } else {
-          uint32_t vv[4];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const int d = 16 * nb + col;
-            const int ra = slot_token(grp, 2 * e2), rb = slot_token(grp, 2 * e2 + 1);
-            const uint32_t lo = vbuf[ra * D + (((d >> 3) ^ v_swizzle(ra)) << 3) + (d & 7)];
-            const uint32_t hi = vbuf[rb * D + (((d >> 3) ^ v_swizzle(rb)) << 3) + (d & 7)];
-            vv[e2] = lo | (hi << 16);
-          }
-          vop = uint4_t{vv[0], vv[1], vv[2], vv[3]};
-        }
+        // ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+        // element i % 4 of the 8-byte loads of lanes 4 e + i / 4 (e = 0..3).
+        // Lane (col, grp) loads row slot_token(grp, col / 4) (then the same
+        // token + 16) at d = 16 nb + 4 (col % 4), so it receives
+        // V[slot_token(grp, e)][16 nb + col]: its V^T operand row.
+        const int d0 = 16 * nb + 4 * (col & 3);
+        const int r0 = slot_token(grp, col >> 2), r1 = r0 + 16;
+        typedef short short4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
+            const_cast<uint16_t*>(vbuf) + r0 * D + (((d0 >> 3) ^ v_swizzle(r0)) << 3) + (d0 & 7)));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(
+            const_cast<uint16_t*>(vbuf) + r1 * D + (((d0 >> 3) ^ v_swizzle(r1)) << 3) + (d0 & 7)));
+        const uint2_t l2 = __builtin_bit_cast(uint2_t, lo), h2 = __builtin_bit_cast(uint2_t, hi);
+        const uint4_t vop{l2.x, l2.y, h2.x, h2.y};
         acc[nb] *= alpha;
         acc[nb] = DT::mfma(vop, phi4, acc[nb]);
         acc[nb] = DT::mfma(vop, plo4, acc[nb]);
@@ -617,21 +587,21 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   //      so a wave never has more than one tile of loads outstanding (at
   //      d = 256 with the row layouts, one tile plus the K half of the next).
   int n = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
-  // V buffers: with kVdma (row layouts) tile A stages into vt and tile B into
-  // the wave's second tile (with KD each V tile is followed by its K tile);
-  // otherwise both stage through registers into vt
+  // V buffers (row layouts): tile A stages into vt and tile B into the wave's
+  // second tile (with KD each V tile is followed by its K tile); the x-split
+  // layout stages nothing
   uint16_t* const vbA = vt;
-  uint16_t* const vbB = (!XS && kVdma) ? vt + (KD ? 2 : 1) * Geo<D>::V_TILE : vt;
-  if constexpr (D > 128 && !(kVdma && !XS)) {
-    // d = 256 with V in registers: one register tile (32 KB of K/V per wave).
-    // A wave waits for each tile; the other waves of the CU keep 3 x 32 KB in
-    // flight meanwhile.
+  uint16_t* const vbB = XS ? vt : vt + (KD ? 2 : 1) * Geo<D>::V_TILE;
+  if constexpr (D > 128 && XS) {
+    // d = 256, x-split: V goes to registers, so one register tile (32 KB of
+    // K/V per wave).  A wave waits for each tile; the other waves of the CU
+    // keep 3 x 32 KB in flight meanwhile.
     Tile A;
     for (int tb = t0; n > 0; --n, tb += kTile) {
       load(A, tb, vbA);
       compute(A, tb, vbA);
     }
-  } else if (D > 128 && !XS && kVdma && n > 0) {
+  } else if (D > 128 && n > 0) {
     // d = 256: K one tile further ahead than V, in three register tiles (V
     // keeps its two LDS tiles, all the LDS four such waves can have).  Before
     // tile t is computed, V(t+1) and K(t+2) are issued, and the wait for tile t

@@ -55,6 +55,27 @@ def test_edge_lengths_all_policies(gq, dtype, d):
         assert_close(got, ref, dtype, what=f"edges {dtype} d={d} {name}")
 
 
+@pytest.mark.parametrize("layout", ["paged", "contiguous"])
+def test_d256_every_tile_count(gq, layout):
+    """At d = 256 the token loop keeps K two tiles ahead and walks the tiles in
+    groups of six with a ragged end: whole sequences of 1 to 14 tiles (and a
+    ragged last tile), one wave per KV head and no split, reach every end of
+    that loop; the all-split policies cut the same sequences into segments of
+    every short length."""
+    lengths = [32 * n + r for n in range(15) for r in (0, 5) if 32 * n + r > 0]
+    if layout == "paged":
+        case = W.paged_case("d256_tiles", 700, lengths, h_q=8, h_kv=4, d=256, dtype=W.BF16,
+                            extra_blocks=2)
+    else:
+        case = W.contiguous_case("d256_tiles_c", 701, 2, 8, 4, 256, 32 * 13 + 5, W.BF16)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name in ("balanced_no_split", "balanced_all_split", "all_single", "all_split_p96"):
+        print(f"d256 tile counts {layout} policy={name}", flush=True)
+        got = run_case(dev, policy=_policies(gq)[name])
+        assert_close(got, ref, W.BF16, what=f"d256 tile counts {layout} {name}")
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
 def test_group_sizes(gq, G):
     h_kv = 2
