@@ -246,9 +246,10 @@ def test_named_workloads_sampled(gq, name):
              if case.kv_bytes <= (1 << 27) else _sample_heads(case, rng, 6, 6))
     ref = R.decode(case, heads=heads)
     dev = case_to_device(case, DEV)
-    for pname in ("default", "balanced_all_split", "pages"):
+    pols = dict(_policies(gq), fused=gq.policy_default(flags=gq.GQA_POLICY_FUSED_MERGE))
+    for pname in ("default", "balanced_all_split", "pages", "fused"):
         print(f"workload {name} policy={pname} rows={len(heads)}", flush=True)
-        got = run_case(dev, policy=_policies(gq)[pname])
+        got = run_case(dev, policy=pols[pname])   # (a fused call's own workspace starts zeroed)
         assert np.all(np.isfinite(got)), pname
         assert_close(got, ref, case.dtype, what=f"{name} {pname}")
 
