@@ -37,8 +37,11 @@
 // (ds_read_b64_tr_b16); the x-split layout stores V transposed already.  Every
 // wave keeps the next tile's K and V loads in flight while it computes the
 // current one, and issues them only once the current tile has landed (one
-// tile of loads outstanding per wave; the x-split layout at d = 256 keeps one
-// tile and no prefetch).  K and V are read once, with non-temporal loads.
+// tile of loads outstanding per wave; at d = 256 with the row layouts K runs
+// one more tile ahead, and the x-split layout at d = 256 keeps one tile and no
+// prefetch).  Where a wave reads only one KV head's slice of each token row,
+// K goes through LDS as well (KD).  K and V are read once, with non-temporal
+// loads.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -194,10 +197,10 @@ __device__ __forceinline__ int seq_tiles(int L) { return max(1, (L + kTile - 1) 
 
 // Waits until every vector-memory operation of this wave has completed
 // (s_waitcnt vmcnt(0); the LDS/scalar and export counters are left alone).
-// The token loop calls it before issuing the next tile: on MI355X a wave with
-// two tiles of 16-byte loads outstanding (up to 32 per lane) streams slower
-// than one that keeps at most one tile (16) in flight, and the CU's other
-// waves cover the gap.
+// The d <= 128 token loop calls it before issuing the next tile: on MI355X a
+// wave with two tiles of 16-byte loads outstanding there (up to 32 per lane)
+// streams slower than one that keeps at most one tile (16) in flight, and the
+// CU's other waves cover the gap.
 __device__ __forceinline__ void wait_tile_loads() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt 0, expcnt 7, lgkmcnt 15 (no wait)
@@ -270,10 +273,9 @@ struct Geo {
 // 16 l), double-buffered so that the next tile's V lands while the current
 // one is read; the matrix-core operand V^T is then read back with the
 // transposing LDS read ds_read_b64_tr_b16.  No V passes through registers.
-
-// LDS of one wave of the matrix-core segment code, in uint16: its V tiles
-// (row layouts), each followed by its K tile when K also goes through LDS
-// (KD), or one tile for the sub-wave state exchange (x-split).
+// The LDS of one wave of the matrix-core segment code, in uint16, is thus its
+// two V tiles (row layouts), each followed by its K tile when K also goes
+// through LDS (KD), or one tile for the sub-wave state exchange (x-split).
 template <int D, bool XS, bool KD = false>
 __host__ __device__ constexpr int wave_lds_elems() {
   return (XS ? 1 : 2) * (KD ? 2 : 1) * Geo<D>::V_TILE;
