@@ -1310,6 +1310,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   __shared__ int32_t wave_tot[kMaxHeadsPerGroup];
   __shared__ float2 mlx[kMaxHeadsPerGroup * 16];                     // sub-wave (m, l) exchange
   __shared__ int last_of_range;                                      // fused merge
+  __shared__ int first_seq;                                          // paged: the share's first sequence
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;                // = hpw * wph
@@ -1323,8 +1324,12 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   uint16_t* const vt = smem + w * tile_elems;
   int32_t* const pref = reinterpret_cast<int32_t*>(smem + nw * tile_elems);
 
-  // ---- paged: pref[s] = n_groups * (tiles of sequences < s); arithmetic when contiguous
-  int64_t total;
+  // ---- paged: pref[s] = n_groups * (tiles of sequences < s); arithmetic when
+  // contiguous.  The host keeps every tile count of a balanced launch below
+  // 2^30, so the share arithmetic below divides in 32 bits (a 64-bit division
+  // is a long instruction sequence, and this prologue runs before a
+  // workgroup's first K/V load).
+  uint32_t total;
   if constexpr (PAGED) {
     int32_t run = 0;
     for (int base = 0; base < a.num_seqs; base += blockDim.x) {
@@ -1351,27 +1356,35 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
     __syncthreads();
     total = __builtin_amdgcn_readfirstlane(run);
   } else {
-    total = (int64_t)a.num_seqs * a.n_groups * seq_tiles(a.s_kv);
+    total = (uint32_t)a.num_seqs * a.n_groups * seq_tiles(a.s_kv);
   }
 
-  const int64_t chunk = max((total + gridDim.x - 1) / gridDim.x, (int64_t)kMinChunkTiles);
+  // share size (a contiguous cache's is the host's, which the merge uses too)
+  const uint32_t chunk32 =
+      PAGED ? max((total + gridDim.x - 1) / gridDim.x, (uint32_t)kMinChunkTiles) : (uint32_t)a.pchunk;
+  const int64_t chunk = chunk32;
   const int64_t x0 = (int64_t)blockIdx.x * chunk;
   if (x0 >= total) return;                       // uniform: no share
-  const int64_t x1 = min(x0 + chunk, total);
+  const int64_t x1 = min(x0 + chunk, (int64_t)total);
 
-  // ---- first sequence whose ranges reach past x0 (largest s with prefix <= x0)
-  int s = 0;
-  {
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (range_prefix<PAGED>(a, pref, mid) <= x0) lo = mid; else hi = mid - 1;
-    }
-    s = lo;
+  // ---- first sequence whose ranges reach past x0 (the s with pref[s] <= x0 <
+  // pref[s + 1]; pref rises by at least n_groups per sequence, so exactly one)
+  int s, hg, L, nt;
+  if constexpr (PAGED) {
+    for (int t = threadIdx.x; t < a.num_seqs; t += blockDim.x)
+      if (pref[t] <= x0 && x0 < pref[t + 1]) first_seq = t;
+    __syncthreads();
+    s = __builtin_amdgcn_readfirstlane(first_seq);
+    L = seq_len<PAGED>(a, s);
+    nt = seq_tiles(L);
+    hg = (int)((uint32_t)(x0 - range_prefix<PAGED>(a, pref, s)) / (uint32_t)nt);
+  } else {
+    L = a.s_kv;
+    nt = seq_tiles(L);
+    const uint32_t per_seq = (uint32_t)a.n_groups * nt;   // tiles of one sequence
+    s = (int)((uint32_t)x0 / per_seq);
+    hg = (int)(((uint32_t)x0 - (uint32_t)s * per_seq) / (uint32_t)nt);
   }
-  int L = seq_len<PAGED>(a, s);
-  int nt = seq_tiles(L);
-  int hg = (int)((x0 - range_prefix<PAGED>(a, pref, s)) / nt);
   const int wg = blockIdx.x;
   const int heads = a.hpw * a.ncol;              // partial rows per slot: (KV head, column)
 
@@ -1410,7 +1423,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
         if (complete) {
           if (a.desc) a.desc[r] = make_int4(wg, wg, -1, 0);
         } else if (t0 == 0) {
-          a.desc[r] = make_int4(wg, (int)((re - 1) / chunk), slot, 0);
+          a.desc[r] = make_int4(wg, (int)((uint32_t)(re - 1) / chunk32), slot, 0);
         }
       }
       if (FUSED && !complete) {
@@ -1423,8 +1436,8 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
         // the XCD): each wave waits until its stores have completed, the
         // barrier then orders them before thread 0's device-scope atomic, and
         // the merging waves issue their loads only after that atomic returned.
-        const int wg0 = (int)(rs / chunk);       // the range's first and last shares
-        const int n = (int)((re - 1) / chunk) - wg0 + 1;
+        const int wg0 = (int)((uint32_t)rs / chunk32);   // the range's first and last shares
+        const int n = (int)((uint32_t)(re - 1) / chunk32) - wg0 + 1;
         wait_tile_loads();                       // vmcnt(0): loads and stores
         __syncthreads();
         if (threadIdx.x == 0)
