@@ -120,6 +120,25 @@ struct BF16 {
 
 // ------------------------------------------------------------ parameters --
 
+// Division by a runtime divisor d >= 1 as a multiply and a shift, exact for
+// numerators below 2^30: shift s = 30 + ceil(log2 d) and multiplier
+// m = ceil(2^s / d) <= 2^31 (the round-up method of Granlund and Montgomery).
+// The kernels' index arithmetic divides by sizes the host knows, and a
+// hardware division is a long instruction sequence on the path to the first
+// load.
+struct FastDiv {
+  uint32_t m;
+  int s;
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (uint32_t)(((uint64_t)n * m) >> s);
+  }
+};
+inline FastDiv fast_div(uint32_t d) {
+  int l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  return FastDiv{(uint32_t)(((uint64_t(1) << (30 + l)) + d - 1) / d), 30 + l};
+}
+
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -151,9 +170,12 @@ struct Params {
   int part_size;                // fixed mode: tokens per partition
   int v1_max_ctx;               // sequences this short are never split
   int max_parts;                // fixed mode: partition slots per (sequence, query head)
-  int pchunk;                   // balanced mode, contiguous: tiles per workgroup share,
-  uint32_t pchunk_m;            //   and n / pchunk = (n * pchunk_m) >> pchunk_s for n < 2^30
-  int pchunk_s;
+  int pchunk;                   // balanced mode, contiguous: tiles per workgroup share
+  FastDiv pchunk_div;           //   and division by it
+  FastDiv rows_div;             // division by T_q * h_q (query rows per sequence)
+  FastDiv hq_div;               // division by h_q
+  FastDiv g_div;                // division by G
+  FastDiv hpw_div;              // division by hpw
   float c;                      // scale * log2(e)
 };
 
@@ -333,7 +355,7 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   bool seg_empty = false;
   if constexpr (SPLIT) {
     w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    sub = w / a.hpw;
+    sub = (int)a.hpw_div.div(w);
     const int n_all = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
     const int u0 = t0 + kTile * (sub * n_all / a.wph);
     const int u1 = min(t1, t0 + kTile * ((sub + 1) * n_all / a.wph));
@@ -346,8 +368,8 @@ __device__ __forceinline__ void wave_segment(const Params& a, uint16_t* smem, ui
   const int G = a.group;
   // column col < ncol is query token tau = col / G, query head j G + col % G
   const bool live = col < a.ncol;
-  const int64_t qo_row = ((int64_t)s * a.tq + (live ? col / G : 0)) * a.h_q + j * G +
-                         (live ? col % G : 0);
+  const int tau = live ? (int)a.g_div.div(col) : 0;
+  const int64_t qo_row = ((int64_t)s * a.tq + tau) * a.h_q + j * G + (live ? col - tau * G : 0);
 
   // ---- Q^T operand: lane holds q[head col][8 d of chunk kk*4+grp]; zero rows pad G to 16
   uint4_t qop[KK];
@@ -833,7 +855,8 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
     const int h = i * RPI + grp;
     uint4_t v{0u, 0u, 0u, 0u};
     if (h < a.ncol) {
-      const int64_t row = ((int64_t)s * a.tq + h / G) * a.h_q + j * G + h % G;
+      const int tau = (int)a.g_div.div(h);
+      const int64_t row = ((int64_t)s * a.tq + tau) * a.h_q + j * G + (h - tau * G);
       v = *reinterpret_cast<const uint4_t*>(a.q + row * D + 8 * col);
     }
     *reinterpret_cast<uint4_t*>(qs + h * (D / 2) + 4 * col) = v;
@@ -1045,7 +1068,8 @@ __device__ __forceinline__ void wave_segment_dot2(const Params& a, uint16_t* vt,
     if (h >= a.ncol) continue;
     const float lh = pick4(l_all + 4 * i, grp);
     if (complete) {
-      const int64_t row = ((int64_t)s * a.tq + h / G) * a.h_q + j * G + h % G;
+      const int tau = (int)a.g_div.div(h);
+      const int64_t row = ((int64_t)s * a.tq + tau) * a.h_q + j * G + (h - tau * G);
       uint4_t w{0u, 0u, 0u, 0u};
       if (!seg_empty) {
 #pragma unroll
@@ -1176,7 +1200,8 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_fixed_k
   const int rest = blockIdx.x / a.max_parts;
   const int hg = rest % a.n_groups;
   const int s = rest / a.n_groups;
-  fixed_item<DT, D, false, XS, NT, SPLIT>(a, smem, mlx, w, s, hg * a.hpw + (SPLIT ? w % a.hpw : w), p);
+  const int wj = SPLIT ? w - (int)a.hpw_div.div(w) * a.hpw : w;   // the wave's head in the group
+  fixed_item<DT, D, false, XS, NT, SPLIT>(a, smem, mlx, w, s, hg * a.hpw + wj, p);
 }
 
 // Paged cache: items blockIdx.x, blockIdx.x + grid, ... of the planner's list.
@@ -1205,6 +1230,7 @@ __global__ __launch_bounds__(kFixedPagedWaves * 64) void partition_fixed_paged_k
     const int code = __builtin_amdgcn_readfirstlane(it.y);
     Params b = a;
     b.hpw = 1 << (code & 3);                       // heads of this item
+    b.hpw_div = FastDiv{1u << 30, 30 + (code & 3)};   // (fast_div of a power of two)
     b.wph = kFixedPagedWaves >> (code & 3);        // waves per head
     fixed_item<DT, D, true, XS, true, true, fixed_paged_kd(D, XS)>(b, smem, mlx, w, s,
                                                                   j0 + w % b.hpw, code >> 2);
@@ -1268,7 +1294,8 @@ __device__ __forceinline__ void fused_range_merge(const Params& a, int s, int hg
     // partial row -> output row: KV head j = hg * hpw + row / ncol, column c = tau * G + g
     const int c = row % a.ncol;
     const int j = hg * a.hpw + row / a.ncol;
-    uint16_t* dst = a.out + (((int64_t)s * a.tq + c / a.group) * a.h_q + j * a.group + c % a.group) * D;
+    const int tau = (int)a.g_div.div(c);
+    uint16_t* dst = a.out + (((int64_t)s * a.tq + tau) * a.h_q + j * a.group + (c - tau * a.group)) * D;
 #pragma unroll
     for (int e2 = 0; e2 < E / 2; ++e2)
       reinterpret_cast<uint32_t*>(dst + r * E)[e2] =
@@ -1387,13 +1414,14 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
   }
   const int wg = blockIdx.x;
   const int heads = a.hpw * a.ncol;              // partial rows per slot: (KV head, column)
+  const int wj = SPLIT ? w - (int)a.hpw_div.div(w) * a.hpw : w;   // the wave's head in the group
 
   for (;;) {
     const int64_t rs = range_prefix<PAGED>(a, pref, s) + (int64_t)hg * nt;
     if (rs >= x1) break;
     const int64_t re = rs + nt;
     const int r = s * a.n_groups + hg;
-    const int j = hg * a.hpw + (SPLIT ? w % a.hpw : w);
+    const int j = hg * a.hpw + wj;
     // This workgroup's part of the range: nothing (an unsplit range it does not
     // own), the whole range (written directly), or one segment of a split range
     // (a partial).  One call site keeps a single copy of the segment code.
@@ -1410,7 +1438,7 @@ __global__ __launch_bounds__(max_heads_per_group(D) * 64) void partition_balance
       slot = 2 * wg + (rs <= x0 ? 0 : 1);
     }
     if (run) {
-      const int64_t hrow = (int64_t)slot * heads + (SPLIT ? w % a.hpw : w) * a.ncol;
+      const int64_t hrow = (int64_t)slot * heads + wj * a.ncol;
       float2* const pml = complete ? nullptr : a.part_ml + hrow;
       float* const po = complete ? nullptr : a.part_o + hrow * D;
       if constexpr (VC > 0)
@@ -1497,8 +1525,8 @@ __device__ __forceinline__ int4 contiguous_record(const Params& a, int r) {
   const uint32_t nt = (uint32_t)seq_tiles(a.s_kv);
   const uint32_t chunk = (uint32_t)a.pchunk;
   const uint32_t rs = (uint32_t)r * nt;
-  const int wg0 = (int)(((uint64_t)rs * a.pchunk_m) >> a.pchunk_s);
-  const int wg1 = (int)(((uint64_t)(rs + nt - 1) * a.pchunk_m) >> a.pchunk_s);
+  const int wg0 = (int)a.pchunk_div.div(rs);
+  const int wg1 = (int)a.pchunk_div.div(rs + nt - 1);
   if (a.s_kv <= a.v1_max_ctx || wg0 == wg1) return make_int4(wg0, wg0, -1, 0);
   return make_int4(wg0, wg1, 2 * wg0 + (rs == (uint32_t)wg0 * chunk ? 0 : 1), 0);
 }
@@ -1534,19 +1562,21 @@ __global__ __launch_bounds__(merge_block(SPI)) void merge_kernel(Params a) {
   int64_t base = 0;
   int4 d{0, 0, 0, 0};
   const int rows_per_seq = a.tq * a.h_q;
-  if (item < a.num_seqs * rows_per_seq) {
-    s = item / rows_per_seq;
-    const int tau = (item % rows_per_seq) / a.h_q;
-    const int i = item % a.h_q;
-    const int j = i / a.group;                    // KV head
-    const int c = tau * a.group + i % a.group;    // column of KV head j's partial rows
+  if (item < a.num_seqs * rows_per_seq) {        // (the host keeps this below 2^30)
+    s = (int)a.rows_div.div(item);
+    const int rem = item - s * rows_per_seq;      // tau * h_q + i
+    const int tau = (int)a.hq_div.div(rem);
+    const int i = rem - tau * a.h_q;
+    const int j = (int)a.g_div.div(i);            // KV head
+    const int c = tau * a.group + (i - j * a.group);   // column of KV head j's partial rows
     if constexpr (BALANCED) {
+      const int hg = (int)a.hpw_div.div(j);       // head group
       if constexpr (PAGED)
-        d = a.desc[s * a.n_groups + j / a.hpw];
+        d = a.desc[s * a.n_groups + hg];
       else
-        d = contiguous_record(a, s * a.n_groups + j / a.hpw);
+        d = contiguous_record(a, s * a.n_groups + hg);
       n = d.y == d.x ? 0 : d.y - d.x + 1;
-      local = (j % a.hpw) * a.ncol + c;
+      local = (j - hg * a.hpw) * a.ncol + c;
     } else {
       const int L = seq_len<PAGED>(a, s);
       n = L <= a.v1_max_ctx ? 0 : (L + a.part_size - 1) / a.part_size;
@@ -2001,13 +2031,8 @@ gqa_status_t launch_typed(const Params& prm, const Plan& pl, int phases, hipStre
       const int64_t total = (int64_t)prm.num_seqs * pl.n_groups *
                             std::max<int64_t>(1, ((int64_t)prm.s_kv + kTile - 1) / kTile);
       const int64_t chunk = std::max<int64_t>((total + grid_b - 1) / grid_b, kMinChunkTiles);
-      // division by chunk for numerators below 2^30: shift s = 30 + ceil(log2 chunk) and
-      // multiplier ceil(2^s / chunk) < 2^32 (the round-up method of Granlund and Montgomery)
-      int l = 0;
-      while ((int64_t(1) << l) < chunk) ++l;
       local.pchunk = (int)chunk;
-      local.pchunk_s = 30 + l;
-      local.pchunk_m = (uint32_t)(((uint64_t(1) << (30 + l)) + chunk - 1) / chunk);
+      local.pchunk_div = fast_div((uint32_t)chunk);
     }
   }
   if (phases & 1) {
@@ -2136,7 +2161,8 @@ gqa_status_t run(const Problem& pb) {
   if ((pol.flags & GQA_POLICY_VALU_DOT2) && !pl.balanced) return GQA_ERR_UNSUPPORTED;
   if (!pl.balanced && (int64_t)pl.max_parts * pb.h_kv * pb.num_seqs > INT32_MAX)
     return GQA_ERR_BAD_SHAPE;
-  if ((int64_t)pb.h_q * pb.tq * pb.num_seqs > INT32_MAX) return GQA_ERR_BAD_SHAPE;
+  // query rows below 2^30: the kernels split row indices with FastDiv
+  if ((int64_t)pb.h_q * pb.tq * pb.num_seqs >= (int64_t(1) << 30)) return GQA_ERR_BAD_SHAPE;
   if (pb.num_seqs == 0) return GQA_OK;
 
   // ---- pointers
@@ -2196,6 +2222,10 @@ gqa_status_t run(const Problem& pb) {
     }
   }
   prm.c = pb.scale * kLog2e;
+  prm.rows_div = fast_div((uint32_t)(pb.tq * pb.h_q));
+  prm.hq_div = fast_div((uint32_t)pb.h_q);
+  prm.g_div = fast_div((uint32_t)G);
+  prm.hpw_div = fast_div((uint32_t)pl.hpw);
   hipStream_t st = static_cast<hipStream_t>(pb.stream);
   char* scr = nullptr;
   if (pb.noalloc) {

@@ -44,7 +44,10 @@
  * streams with distinct workspaces and outputs may run concurrently.
  *
  * Errors.  Every argument is checked on the host before any HIP call; a
- * failed check returns its status with nothing launched.  A failed launch
+ * failed check returns its status with nothing launched.  Sizes:
+ * num_seqs * T_q * h_q must be below 2^30 and the longest context
+ * (max_blocks_per_seq * block_size, or s_kv) at most 2^30 tokens; larger ones
+ * return GQA_ERR_BAD_SHAPE.  A failed launch
  * returns GQA_ERR_LAUNCH.  Faults during execution surface at the caller's
  * next synchronisation of the stream.  Device-resident data the host cannot
  * see is handled as follows: ctx_lens[s] is clamped to

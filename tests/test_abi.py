@@ -111,6 +111,7 @@ ERR = dict(NULL=1, SHAPE=2, UNSUP=3, ALIGN=4, WS=5, POLICY=6, SCALE=7)
     (dict(num_seqs=-1), "SHAPE"),
     (dict(max_blocks=0), "SHAPE"),
     (dict(max_blocks=1 << 27, bs=16), "SHAPE"),
+    (dict(num_seqs=1 << 27, h_q=8), "SHAPE"),          # 2^30 query rows
     (dict(d=96), "UNSUP"),
     (dict(d=512), "UNSUP"),
     (dict(d=32), "UNSUP"),
