@@ -178,7 +178,8 @@ size_t gqa_decode_workspace_size(int num_seqs, int h_q, int h_kv, int d_head, in
  * scale multiplies the logits (the workloads use 1 / sqrt(d_head)).  stream
  * is a hipStream_t (NULL: the default stream).  workspace may be NULL when
  * gqa_decode_workspace_size() is 0.  num_seqs == 0 returns GQA_OK and
- * launches nothing.
+ * launches nothing.  k_cache and v_cache must not be NULL, even when every
+ * sequence is empty (the host cannot see ctx_lens): GQA_ERR_NULL_PTR.
  */
 gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_table, const int32_t* ctx_lens, void* out,

@@ -59,8 +59,11 @@ def _case(c):
     if c["layout"] == "contiguous":
         return W.contiguous_case("rnd", c["seed"], len(c["lens"]), c["G"] * c["h_kv"], c["h_kv"],
                                  c["d"], max(c["lens"]), c["dtype"], scale=c["scale"], t_q=c["t_q"])
+    # a paged pool holds at least one block: the library takes no NULL pool, even
+    # when every sequence is empty
+    extra = max(c["extra"], 1 if max(c["lens"]) == 0 else 0)
     case = W.paged_case("rnd", c["seed"], c["lens"], h_q=c["G"] * c["h_kv"], h_kv=c["h_kv"],
-                        d=c["d"], dtype=c["dtype"], block_size=c["bs"], extra_blocks=c["extra"],
+                        d=c["d"], dtype=c["dtype"], block_size=c["bs"], extra_blocks=extra,
                         scale=c["scale"], t_q=c["t_q"])
     return W.xsplit_case(case) if c["layout"] == "xsplit" else case
 
