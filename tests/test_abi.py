@@ -126,6 +126,8 @@ ERR = dict(NULL=1, SHAPE=2, UNSUP=3, ALIGN=4, WS=5, POLICY=6, SCALE=7)
     (dict(out=None), "NULL"),
     (dict(bt=None), "NULL"),
     (dict(ctx=None), "NULL"),
+    (dict(k=None), "NULL"),                          # a paged pool is never NULL
+    (dict(v=None), "NULL"),
     (dict(q=MIS), "ALIGN"),
     (dict(k=MIS), "ALIGN"),
     (dict(out=MIS), "ALIGN"),
