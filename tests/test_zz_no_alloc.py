@@ -5,7 +5,8 @@ CPU part: the header's scratch size matches the binding, and the host checks
 that refuse a call before any HIP call.  GPU part: two calls in a row, the
 second on a smaller input, each equal bit for bit to gqa_decode's output with
 a caller-owned workspace on the same inputs (same kernels, same grid) and
-within the oracle's tolerance."""
+within the oracle's tolerance; and a call captured in a HIP graph, replayed
+several times."""
 import ctypes
 import os
 import re
@@ -103,3 +104,35 @@ def test_noalloc_d256_and_phases(gq):
                       policy=gq.Policy(pol.partition_size, pol.v1_max_ctx, 2, 0))
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), want)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("pname", ["default", "pages"])
+def test_noalloc_graph_replay(gq, pname):
+    """The callers this entry point is for include HIP-graph capture: a captured
+    call, replayed several times with eager work and synchronisations between
+    the replays, gives the eager call's bits every time (the graph holds the
+    library's kernels only; nothing in it clears memory)."""
+    policy = None if pname == "default" else gq.policy_pages()
+    case = W.paged_case("na_graph", 2103, [6000, 1, 900, 15000, 64], h_q=32, h_kv=8, d=128,
+                        dtype=W.F16, extra_blocks=1)
+    dev = case_to_device(case, DEV)
+    stream = torch.cuda.Stream(device=DEV)
+    args = (dev["q"], dev["k"], dev["v"], dev["block_table"], dev["ctx_lens"])
+    with torch.cuda.stream(stream):
+        out = torch.zeros_like(dev["q"])
+        gq.decode_noalloc(*args, out, scale=case.scale, policy=policy, stream=stream)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            gq.decode_noalloc(*args, out, scale=case.scale, policy=policy, stream=stream)
+        for rep in range(4):
+            print(f"noalloc graph policy={pname} replay {rep}", flush=True)
+            out.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {rep}"
+    assert_close(eager.float().cpu().numpy().astype(np.float64), R.decode(case), W.F16,
+                 what=f"noalloc graph {pname}")
