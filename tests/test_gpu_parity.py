@@ -306,6 +306,19 @@ def test_long_sequence_many_segments(gq):
     assert_close(got, ref, W.F16, what="S=70001 fixed 64")
 
 
+def test_million_token_sequence(gq):
+    """One paged sequence of 2^20 + 5 tokens (the balanced shares cut it into
+    hundreds of partials per head; the pages' 512-token partitions into 2049)."""
+    n = (1 << 20) + 5
+    case = W.paged_case("mega", 1500, [n, 3], h_q=8, h_kv=1, d=64, dtype=W.F16)
+    ref = R.decode(case)
+    dev = case_to_device(case, DEV)
+    for name in ("default", "pages"):
+        print(f"million-token sequence policy={name}", flush=True)
+        got = run_case(dev, policy=_policies(gq)[name])
+        assert_close(got, ref, W.F16, what=f"2^20 tokens {name}")
+
+
 @pytest.mark.parametrize("pname", ["default", "pages"])
 def test_graph_replay_matches_eager(gq, pname):
     """Decode steps captured in a HIP graph: every replay, with eager work and
