@@ -8,7 +8,8 @@ the replay times the steps themselves (both sides bracketed by
 synchronisations).  The output after the timed replay must equal an eager
 step's bit for bit.  K/V are cycled over enough device copies (>= 1 GiB in
 total, i.e. more than four times the 256 MB Infinity Cache) that no step can be
-served from the cache a previous step filled.
+served from the cache a previous step filled; a pool under 16 MB (the
+launch-bound tiny workload) is cycled over 64 copies only.
 
 Prints ONE JSON line.  The headline workload is mixed_b256, the largest
 configuration (256 sequences of log-normal lengths, both single-pass and split
@@ -43,6 +44,7 @@ sys.path.insert(0, ROOT)
 METRIC = "K/V HBM GB/s (and % of peak) + decode attention µs/step, 1 GPU"
 PEAK_GBS = 8000.0                       # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30                  # K/V bytes cycled per step sequence
+MAX_COPIES = 64                         # K/V copies at most (each is a device copy to make)
 HEADLINE = "mixed_b256"            # the largest configuration (256 sequences, mixed lengths)
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_08_amd", "csrc", "gqa_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -126,7 +128,7 @@ def time_workload(case, policy_name: str, steps: int, warmup: int):
     k0 = bits_to_device(case.k, case.dtype, dev)
     v0 = bits_to_device(case.v, case.dtype, dev)
     pool_bytes = 2 * k0.numel() * k0.element_size()
-    copies = max(2, math.ceil(ROTATE_BYTES / max(1, pool_bytes)))
+    copies = max(2, min(MAX_COPIES, math.ceil(ROTATE_BYTES / max(1, pool_bytes))))
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     stream = torch.cuda.Stream(device=dev)
